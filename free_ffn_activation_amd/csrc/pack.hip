@@ -1,0 +1,158 @@
+// Offline kernels: proxy packing, layout transforms, workspace fill and the
+// digit histograms used by calibration.
+//
+// Packing ([blog] = deep-dive blog "Prox 完全拆解", section "Stage 1": the up
+// and gate proxies are symmetric per-row INT4 copies kept resident on the GPU;
+// W_down has none).  A row is a row of the [d_model, d_ff] matrix, i.e. one
+// input coordinate, so Stage 1 reads one contiguous run per kept coordinate.
+// scale = fp32(absmax / 7); code = clamp(rint_half_even(fp32(w / scale)),
+// -7, 7) with IEEE-rounded fp32 divisions; a zero row has scale 0, codes 0.
+#include "prox_device.h"
+#include "prox_internal.h"
+
+namespace prox {
+namespace {
+
+__device__ __forceinline__ int quant_code(float w, float sc) {
+  if (!(sc > 0.f)) return 0;
+  const float q = rintf(__fdiv_rn(w, sc));
+  return static_cast<int>(fminf(7.f, fmaxf(-7.f, q)));
+}
+
+// One block per input row: absmax of the row in both matrices, the two scales,
+// then the packed 16-byte groups (8 bytes up codes, 8 bytes gate codes).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void pack_rows_kernel(const void* wu, const void* wg, int d,
+                                                              int f, uint8_t* q, float* scale) {
+  __shared__ float s_max[2][4];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const size_t rb = static_cast<size_t>(i) * f;
+  float mu = 0.f, mg = 0.f;
+  for (int c = tid; c < f; c += kThreads) {
+    mu = fmaxf(mu, fabsf(load_elem<T>(wu, rb + c)));
+    mg = fmaxf(mg, fabsf(load_elem<T>(wg, rb + c)));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    mu = fmaxf(mu, __shfl_xor(mu, m, 64));
+    mg = fmaxf(mg, __shfl_xor(mg, m, 64));
+  }
+  if ((tid & 63) == 0) {
+    s_max[0][tid >> 6] = mu;
+    s_max[1][tid >> 6] = mg;
+  }
+  __syncthreads();
+  const float au = fmaxf(fmaxf(s_max[0][0], s_max[0][1]), fmaxf(s_max[0][2], s_max[0][3]));
+  const float ag = fmaxf(fmaxf(s_max[1][0], s_max[1][1]), fmaxf(s_max[1][2], s_max[1][3]));
+  const float su = __fdiv_rn(au, 7.0f);
+  const float sg = __fdiv_rn(ag, 7.0f);
+  if (tid == 0) {
+    scale[i] = su;
+    scale[d + i] = sg;
+  }
+  for (int g = tid; g < f / 16; g += kThreads) {
+    uint32_t up[2] = {0u, 0u}, gt[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const size_t c = rb + static_cast<size_t>(g) * 16 + k;
+      const uint32_t nu = static_cast<uint32_t>(quant_code(load_elem<T>(wu, c), su) + 8);
+      const uint32_t ng = static_cast<uint32_t>(quant_code(load_elem<T>(wg, c), sg) + 8);
+      up[k >> 3] |= nu << (4 * (k & 7));
+      gt[k >> 3] |= ng << (4 * (k & 7));
+    }
+    *reinterpret_cast<uint4*>(q + rb + static_cast<size_t>(g) * 16) =
+        make_uint4(up[0], up[1], gt[0], gt[1]);
+  }
+}
+
+// dst[j][which][i] = src[i][j] for src [d][f]; 64x64 tiles through LDS.
+template <typename S>
+__global__ __launch_bounds__(kThreads) void transpose_kernel(const S* __restrict__ src, int d, int f,
+                                                              S* __restrict__ dst, int which) {
+  __shared__ S tile[64][65];
+  const int j0 = blockIdx.x * 64;
+  const int i0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63;
+  const int ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) tile[r][tx] = src[static_cast<size_t>(i0 + r) * f + j0 + tx];
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4)
+    dst[static_cast<size_t>(j0 + r) * 2 * d + static_cast<size_t>(which) * d + i0 + tx] = tile[tx][r];
+}
+
+__global__ void fill_zero_kernel(uint8_t* p, size_t bytes) {
+  const size_t n4 = bytes / 4;
+  uint32_t* p4 = reinterpret_cast<uint32_t*>(p);
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p4[i] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x < (bytes & 3)) p[n4 * 4 + threadIdx.x] = 0;
+}
+
+// Histogram of the 8-bit digit at `shift` of the keys |v| (fp32 bit patterns,
+// sign cleared) whose bits under prefix_mask equal prefix.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void digit_hist_kernel(const void* v, size_t n, uint32_t prefix,
+                                                               uint32_t prefix_mask, int shift,
+                                                               uint32_t* hist) {
+  __shared__ uint32_t h[256];
+  h[threadIdx.x] = 0u;
+  __syncthreads();
+  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride) {
+    const uint32_t key = __float_as_uint(load_elem<T>(v, i)) & 0x7FFFFFFFu;
+    if ((key & prefix_mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], h[threadIdx.x]);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int wdtype,
+                       uint8_t* proxy_q, float* proxy_scale, void* w_upgate_t, hipStream_t s) {
+  const dim3 tgrid(static_cast<unsigned>(f / 64), static_cast<unsigned>(d / 64));
+  if (wdtype == PROX_BF16) {
+    hipLaunchKernelGGL((pack_rows_kernel<Bf16Tag>), dim3(d), dim3(kThreads), 0, s, w_up, w_gate, d, f,
+                       proxy_q, proxy_scale);
+    hipLaunchKernelGGL((transpose_kernel<uint16_t>), tgrid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(w_up), d, f, static_cast<uint16_t*>(w_upgate_t), 0);
+    hipLaunchKernelGGL((transpose_kernel<uint16_t>), tgrid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(w_gate), d, f, static_cast<uint16_t*>(w_upgate_t), 1);
+  } else {
+    hipLaunchKernelGGL((pack_rows_kernel<F32Tag>), dim3(d), dim3(kThreads), 0, s, w_up, w_gate, d, f,
+                       proxy_q, proxy_scale);
+    hipLaunchKernelGGL((transpose_kernel<float>), tgrid, dim3(kThreads), 0, s,
+                       static_cast<const float*>(w_up), d, f, static_cast<float*>(w_upgate_t), 0);
+    hipLaunchKernelGGL((transpose_kernel<float>), tgrid, dim3(kThreads), 0, s,
+                       static_cast<const float*>(w_gate), d, f, static_cast<float*>(w_upgate_t), 1);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  size_t blocks = (bytes / 4 + kThreads - 1) / kThreads;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
+                     static_cast<uint8_t*>(p), bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_digit_histogram(const void* v, size_t n, int vdtype, uint32_t prefix,
+                                  uint32_t prefix_mask, int shift, uint32_t* hist, hipStream_t s) {
+  size_t blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks == 0) blocks = 1;
+  if (vdtype == PROX_BF16)
+    hipLaunchKernelGGL((digit_hist_kernel<Bf16Tag>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                       0, s, v, n, prefix, prefix_mask, shift, hist);
+  else
+    hipLaunchKernelGGL((digit_hist_kernel<F32Tag>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                       0, s, v, n, prefix, prefix_mask, shift, hist);
+  return hipGetLastError();
+}
+
+}  // namespace prox

@@ -1,0 +1,516 @@
+// Host side of the C ABI declared in include/prox.h: argument validation,
+// launch planning, workspace layout and calibration orchestration.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "prox_internal.h"
+
+#define PROX_API extern "C" __attribute__((visibility("default")))
+
+namespace prox {
+namespace {
+
+thread_local std::string g_err;
+
+prox_status fail(prox_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+prox_status hip_fail(hipError_t e, const char* what) {
+  return fail(PROX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(int wdtype) { return wdtype == PROX_BF16 ? 2 : 4; }
+
+prox_status check_shape(int32_t d, int32_t f, int32_t wdtype) {
+  if (wdtype != PROX_F32 && wdtype != PROX_BF16)
+    return fail(PROX_ERR_INVALID_ARG, "wdtype %d is neither PROX_F32 nor PROX_BF16", wdtype);
+  if (d < 64 || f < 128)
+    return fail(PROX_ERR_INVALID_ARG, "shape d_model=%d d_ff=%d below the minimum 64 x 128", d, f);
+  if (d % 64 != 0 || f % 128 != 0)
+    return fail(PROX_ERR_UNSUPPORTED, "shape d_model=%d d_ff=%d: need d_model %% 64 == 0 and "
+                "d_ff %% 128 == 0", d, f);
+  if (d > 12288 || f > 65536)
+    return fail(PROX_ERR_UNSUPPORTED, "shape d_model=%d d_ff=%d above 12288 x 65536", d, f);
+  return PROX_OK;
+}
+
+prox_status check_layer(const prox_layer* L) {
+  if (L == nullptr) return fail(PROX_ERR_INVALID_ARG, "layer descriptor is NULL");
+  prox_status st = check_shape(L->d_model, L->d_ff, L->wdtype);
+  if (st != PROX_OK) return st;
+  if (L->reserved != 0) return fail(PROX_ERR_INVALID_ARG, "layer->reserved must be 0");
+  if (!L->proxy_q || !L->proxy_scale || !L->w_upgate_t || !L->w_down)
+    return fail(PROX_ERR_INVALID_ARG, "layer buffer pointer is NULL");
+  if (!aligned(L->proxy_q, 16) || !aligned(L->proxy_scale, 16) || !aligned(L->w_upgate_t, 16) ||
+      !aligned(L->w_down, 16))
+    return fail(PROX_ERR_INVALID_ARG, "layer buffers must be 16-byte aligned");
+  return PROX_OK;
+}
+
+prox_status check_tau(float t, const char* name) {
+  if (std::isnan(t) || t < 0.f)
+    return fail(PROX_ERR_INVALID_ARG, "%s = %g: thresholds must be >= 0 or +inf", name,
+                static_cast<double>(t));
+  return PROX_OK;
+}
+
+prox_status check_batch(int32_t batch) {
+  if (batch < 1 || batch > 256) return fail(PROX_ERR_INVALID_ARG, "batch %d outside [1, 256]", batch);
+  return PROX_OK;
+}
+
+prox_status check_ws(const Plan& p, int32_t batch, const void* ws, size_t ws_bytes) {
+  if (ws == nullptr) return fail(PROX_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(PROX_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = p.tok_bytes * static_cast<size_t>(batch);
+  if (ws_bytes < need)
+    return fail(PROX_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  return PROX_OK;
+}
+
+Stage1Args stage1_args(const Plan& p, const prox_layer* L, const void* x, float tau_x, float tau_s,
+                       void* ws, float* s_tilde, int* in_count) {
+  Stage1Args a;
+  a.d = p.d;
+  a.f = p.f;
+  a.splits = p.splits;
+  a.rows_per_split = p.rows_per_split;
+  a.n_panels = p.n_panels;
+  a.proxy_q = static_cast<const uint8_t*>(L->proxy_q);
+  a.proxy_scale = L->proxy_scale;
+  a.x = x;
+  a.tau_x = tau_x;
+  a.tau_s = tau_s;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.tok_bytes = p.tok_bytes;
+  a.off_tickets = p.off_tickets;
+  a.off_kcount = p.off_kcount;
+  a.off_partial = p.off_partial;
+  a.off_bitmap = p.off_bitmap;
+  a.s_tilde = s_tilde;
+  a.in_count = in_count;
+  return a;
+}
+
+UpGateArgs upgate_args(const Plan& p, const prox_layer* L, const void* x, void* ws, int* mask_idx,
+                       int* mask_count, float* y) {
+  UpGateArgs a;
+  a.d = p.d;
+  a.f = p.f;
+  a.max_cpb = p.ug_max_cpb;
+  a.w_upgate_t = L->w_upgate_t;
+  a.x = x;
+  a.ws = static_cast<const uint8_t*>(ws);
+  a.ws_mut = static_cast<uint8_t*>(ws);
+  a.tok_bytes = p.tok_bytes;
+  a.off_bitmap = p.off_bitmap;
+  a.off_ssp = p.off_ssp;
+  a.mask_idx = mask_idx;
+  a.mask_count = mask_count;
+  a.y = y;
+  return a;
+}
+
+DownArgs down_args(const Plan& p, const prox_layer* L, void* ws, const int* mask_idx,
+                   const int* mask_count, float* y) {
+  DownArgs a;
+  a.d = p.d;
+  a.f = p.f;
+  a.col_slices = p.dn_col_slices;
+  a.row_groups = p.dn_row_groups;
+  a.max_rows = p.dn_max_rows;
+  a.w_down = L->w_down;
+  a.ws = static_cast<const uint8_t*>(ws);
+  a.tok_bytes = p.tok_bytes;
+  a.off_ssp = p.off_ssp;
+  a.mask_idx = mask_idx;
+  a.mask_count = mask_count;
+  a.y = y;
+  return a;
+}
+
+prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, float tau_x,
+                        float tau_s, float* y, int32_t* mask_idx, int32_t* mask_count,
+                        int32_t* in_count, void* ws, size_t ws_bytes, void* stream,
+                        void* const* events) {
+  prox_status st = check_layer(layer);
+  if (st != PROX_OK) return st;
+  if ((st = check_batch(batch)) != PROX_OK) return st;
+  if ((st = check_tau(tau_x, "tau_x")) != PROX_OK) return st;
+  if ((st = check_tau(tau_s, "tau_s")) != PROX_OK) return st;
+  if (!x || !y || !mask_idx || !mask_count)
+    return fail(PROX_ERR_INVALID_ARG, "x, y, mask_idx and mask_count must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mask_idx, 4) || !aligned(mask_count, 4) ||
+      (in_count && !aligned(in_count, 4)))
+    return fail(PROX_ERR_INVALID_ARG, "x and y must be 16-byte aligned, index buffers 4-byte aligned");
+  const Plan p = make_plan(layer->d_model, layer->d_ff, layer->wdtype);
+  if ((st = check_ws(p, batch, ws, ws_bytes)) != PROX_OK) return st;
+  if (events) {
+    for (int i = 0; i < 4; ++i)
+      if (!events[i]) return fail(PROX_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  e = launch_stage1(stage1_args(p, layer, x, tau_x, tau_s, ws, nullptr, in_count), layer->wdtype,
+                    batch, false, s);
+  if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
+  if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  e = launch_upgate(upgate_args(p, layer, x, ws, mask_idx, mask_count, y), layer->wdtype, batch,
+                    p.ug_blocks, true, s);
+  if (e != hipSuccess) return hip_fail(e, "stage-2 up/gate launch");
+  if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[2]), s)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, s);
+  if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
+  if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[3]), s)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  return PROX_OK;
+}
+
+// keep-th largest |v| over n values by an MSB-first radix select on the fp32
+// bit patterns of |v| (order-preserving for non-negative floats).  Counting
+// runs on the GPU; the host walks the 256-bin histograms.  Blocks.
+prox_status select_kth_largest(const void* v, size_t n, int vdtype, uint64_t keep,
+                               uint32_t* hist_dev, hipStream_t s, float* out) {
+  if (keep == 0) {
+    *out = INFINITY;
+    return PROX_OK;
+  }
+  uint32_t prefix = 0, pmask = 0;
+  uint64_t remaining = keep;
+  std::vector<uint32_t> hist(256);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hipError_t e = launch_fill_zero(hist_dev, 256 * sizeof(uint32_t), s);
+    if (e != hipSuccess) return hip_fail(e, "histogram clear");
+    e = launch_digit_histogram(v, n, vdtype, prefix, pmask, shift, hist_dev, s);
+    if (e != hipSuccess) return hip_fail(e, "histogram launch");
+    e = hipMemcpyAsync(hist.data(), hist_dev, 256 * sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "histogram copy");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "calibration synchronisation");
+    uint64_t cum = 0;
+    int digit = -1;
+    for (int dg = 255; dg >= 0; --dg) {
+      if (cum + hist[dg] >= remaining) {
+        digit = dg;
+        break;
+      }
+      cum += hist[dg];
+    }
+    if (digit < 0) return fail(PROX_ERR_INTERNAL, "radix select lost its rank (count %llu)",
+                               static_cast<unsigned long long>(cum));
+    remaining -= cum;
+    prefix |= static_cast<uint32_t>(digit) << shift;
+    pmask |= 255u << shift;
+  }
+  uint32_t bits = prefix;
+  float r;
+  std::memcpy(&r, &bits, 4);
+  *out = r;
+  return PROX_OK;
+}
+
+uint64_t keep_count(double keep, uint64_t n) {
+  const double k = std::ceil(keep * static_cast<double>(n));
+  if (!(k > 0.0)) return 0;
+  if (k >= static_cast<double>(n)) return n;
+  return static_cast<uint64_t>(k);
+}
+
+constexpr int kCalChunk = 16;  // calibration tokens per Stage-1 launch
+
+size_t calib_bytes(const Plan& p, int32_t n_tokens) {
+  return align256(static_cast<size_t>(n_tokens) * p.f * sizeof(float)) +
+         p.tok_bytes * std::min<int32_t>(n_tokens, kCalChunk) + 1024;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+Plan make_plan(int d, int f, int wdtype) {
+  Plan p;
+  p.d = d;
+  p.f = f;
+  p.wdtype = wdtype;
+  p.n_panels = f / kPanel;
+  // about three 256-thread blocks per CU over 256 CUs for Stage 1
+  const int target = 768;
+  int splits = static_cast<int>(std::lround(static_cast<double>(target) / p.n_panels));
+  splits = std::max(1, std::min(64, splits));
+  int rps = (d + splits - 1) / splits;
+  rps = (rps + 63) / 64 * 64;
+  rps = std::min(rps, 4096);  // bounds the LDS list of kept rows
+  p.rows_per_split = rps;
+  p.splits = (d + rps - 1) / rps;
+  // up/gate: enough 4-wave blocks for one kept channel per wave at ~30% keep
+  p.ug_blocks = std::max(64, f / 12);
+  p.ug_max_cpb = (f + p.ug_blocks - 1) / p.ug_blocks;
+  // down: column slices of one wave-load, row groups to reach ~768 blocks
+  const int cw = 64 * (16 / static_cast<int>(elem_size(wdtype)));
+  p.dn_col_slices = (d + cw - 1) / cw;
+  int rg = static_cast<int>(std::lround(768.0 / p.dn_col_slices));
+  rg = std::max(1, std::min(f / 4, rg));
+  p.dn_row_groups = rg;
+  p.dn_max_rows = (f + rg - 1) / rg;
+  // per-token workspace slice
+  size_t off = 0;
+  p.off_tickets = off;
+  off = align256(off + static_cast<size_t>(p.n_panels) * 4);
+  p.off_kcount = off;
+  off = align256(off + static_cast<size_t>(p.splits) * 4);
+  p.off_partial = off;
+  off = align256(off + static_cast<size_t>(p.splits) * 2 * f * 4);
+  p.off_bitmap = off;
+  off = align256(off + static_cast<size_t>(f / 32) * 4);
+  p.off_ssp = off;
+  off = align256(off + static_cast<size_t>(f) * 4);
+  p.tok_bytes = off;
+  return p;
+}
+
+}  // namespace prox
+
+using namespace prox;
+
+PROX_API int32_t prox_abi_version(void) { return PROX_ABI_VERSION; }
+
+PROX_API const char* prox_last_error(void) { return g_err.c_str(); }
+
+PROX_API prox_status prox_layer_sizes(int32_t d, int32_t f, int32_t wdtype, size_t* bytes_out) {
+  try {
+    g_err.clear();
+    if (!bytes_out) return fail(PROX_ERR_INVALID_ARG, "bytes_out is NULL");
+    prox_status st = check_shape(d, f, wdtype);
+    if (st != PROX_OK) return st;
+    const size_t es = elem_size(wdtype);
+    bytes_out[0] = static_cast<size_t>(d) * f;
+    bytes_out[1] = static_cast<size_t>(2) * d * sizeof(float);
+    bytes_out[2] = static_cast<size_t>(2) * f * d * es;
+    bytes_out[3] = static_cast<size_t>(f) * d * es;
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_workspace_size(int32_t d, int32_t f, int32_t batch, size_t* bytes) {
+  try {
+    g_err.clear();
+    if (!bytes) return fail(PROX_ERR_INVALID_ARG, "bytes is NULL");
+    prox_status st = check_shape(d, f, PROX_BF16);
+    if (st != PROX_OK) return st;
+    if ((st = check_batch(batch)) != PROX_OK) return st;
+    // the layout does not depend on the weight dtype
+    *bytes = make_plan(d, f, PROX_BF16).tok_bytes * static_cast<size_t>(batch);
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_calibrate_workspace_size(int32_t d, int32_t f, int32_t n_tokens,
+                                                   size_t* bytes) {
+  try {
+    g_err.clear();
+    if (!bytes) return fail(PROX_ERR_INVALID_ARG, "bytes is NULL");
+    prox_status st = check_shape(d, f, PROX_BF16);
+    if (st != PROX_OK) return st;
+    if (n_tokens < 1 || n_tokens > 65536)
+      return fail(PROX_ERR_INVALID_ARG, "n_tokens %d outside [1, 65536]", n_tokens);
+    *bytes = calib_bytes(make_plan(d, f, PROX_BF16), n_tokens);
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    if (!ws) return fail(PROX_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned(ws, 4)) return fail(PROX_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+    hipError_t e = launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "workspace fill");
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_pack_proxy(const void* W_up, const void* W_gate, const void* W_down,
+                                     const prox_layer* out, void* stream) {
+  try {
+    g_err.clear();
+    prox_status st = check_layer(out);
+    if (st != PROX_OK) return st;
+    if (!W_up || !W_gate || !W_down) return fail(PROX_ERR_INVALID_ARG, "input weight pointer is NULL");
+    if (!aligned(W_up, 16) || !aligned(W_gate, 16) || !aligned(W_down, 16))
+      return fail(PROX_ERR_INVALID_ARG, "input weights must be 16-byte aligned");
+    const int d = out->d_model, f = out->d_ff;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_pack(W_up, W_gate, d, f, out->wdtype, static_cast<uint8_t*>(out->proxy_q),
+                               out->proxy_scale, out->w_upgate_t, s);
+    if (e != hipSuccess) return hip_fail(e, "pack launch");
+    if (out->w_down != W_down) {
+      e = hipMemcpyAsync(out->w_down, W_down, static_cast<size_t>(f) * d * elem_size(out->wdtype),
+                         hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "W_down copy");
+    }
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_calibrate(const prox_layer* layer, const void* X_cal, int32_t n_tokens,
+                                    float keep_x, float sparsity_s, float* tau_x, float* tau_s,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    prox_status st = check_layer(layer);
+    if (st != PROX_OK) return st;
+    if (!X_cal || !tau_x || !tau_s) return fail(PROX_ERR_INVALID_ARG, "X_cal, tau_x, tau_s must be non-NULL");
+    if (!aligned(X_cal, 16)) return fail(PROX_ERR_INVALID_ARG, "X_cal must be 16-byte aligned");
+    if (n_tokens < 1 || n_tokens > 65536)
+      return fail(PROX_ERR_INVALID_ARG, "n_tokens %d outside [1, 65536]", n_tokens);
+    if (!(keep_x >= 0.f && keep_x <= 1.f) || !(sparsity_s >= 0.f && sparsity_s <= 1.f))
+      return fail(PROX_ERR_INVALID_ARG, "keep_x and sparsity_s must lie in [0, 1]");
+    const Plan p = make_plan(layer->d_model, layer->d_ff, layer->wdtype);
+    if (!ws || !aligned(ws, 256)) return fail(PROX_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+    const size_t need = calib_bytes(p, n_tokens);
+    if (ws_bytes < need)
+      return fail(PROX_ERR_INVALID_ARG, "calibration workspace of %zu bytes is smaller than the %zu needed",
+                  ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    float* s_all = reinterpret_cast<float*>(base);
+    uint8_t* tws = base + align256(static_cast<size_t>(n_tokens) * p.f * sizeof(float));
+    const int chunk = std::min<int32_t>(n_tokens, kCalChunk);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(tws + p.tok_bytes * chunk);
+    hipError_t e = launch_fill_zero(tws, p.tok_bytes * chunk, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace fill");
+
+    const uint64_t nx = static_cast<uint64_t>(n_tokens) * p.d;
+    float tx = 0.f;
+    st = select_kth_largest(X_cal, nx, layer->wdtype, keep_count(static_cast<double>(keep_x), nx), hist,
+                            s, &tx);
+    if (st != PROX_OK) return st;
+
+    const size_t es = elem_size(layer->wdtype);
+    for (int t0 = 0; t0 < n_tokens; t0 += chunk) {
+      const int nb = std::min(chunk, n_tokens - t0);
+      const void* xt = static_cast<const uint8_t*>(X_cal) + static_cast<size_t>(t0) * p.d * es;
+      e = launch_stage1(stage1_args(p, layer, xt, tx, INFINITY, tws, s_all + static_cast<size_t>(t0) * p.f,
+                                    nullptr),
+                        layer->wdtype, nb, true, s);
+      if (e != hipSuccess) return hip_fail(e, "stage-1 launch (calibration)");
+    }
+    const uint64_t ns = static_cast<uint64_t>(n_tokens) * p.f;
+    const double keep_s = 1.0 - static_cast<double>(sparsity_s);
+    float ts = 0.f;
+    st = select_kth_largest(s_all, ns, PROX_F32, keep_count(keep_s, ns), hist, s, &ts);
+    if (st != PROX_OK) return st;
+    *tau_x = tx;
+    *tau_s = ts;
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_ffn_decode(const prox_layer* layer, const void* x, int32_t batch, float tau_x,
+                                     float tau_s, float* y, int32_t* mask_idx, int32_t* mask_count,
+                                     int32_t* in_count, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    return decode_impl(layer, x, batch, tau_x, tau_s, y, mask_idx, mask_count, in_count, ws, ws_bytes,
+                       stream, nullptr);
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32_t batch,
+                                            float tau_x, float tau_s, float* y, int32_t* mask_idx,
+                                            int32_t* mask_count, int32_t* in_count, void* ws,
+                                            size_t ws_bytes, void* stream, void* const* events) {
+  try {
+    g_err.clear();
+    if (!events) return fail(PROX_ERR_INVALID_ARG, "events is NULL");
+    return decode_impl(layer, x, batch, tau_x, tau_s, y, mask_idx, mask_count, in_count, ws, ws_bytes,
+                       stream, events);
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_ffn_stage2(const prox_layer* layer, const void* x, int32_t batch,
+                                     const int32_t* mask_idx, const int32_t* mask_count, float* y,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    prox_status st = check_layer(layer);
+    if (st != PROX_OK) return st;
+    if ((st = check_batch(batch)) != PROX_OK) return st;
+    if (!x || !y || !mask_idx || !mask_count)
+      return fail(PROX_ERR_INVALID_ARG, "x, y, mask_idx and mask_count must be non-NULL");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mask_idx, 4) || !aligned(mask_count, 4))
+      return fail(PROX_ERR_INVALID_ARG, "x and y must be 16-byte aligned, index buffers 4-byte aligned");
+    const Plan p = make_plan(layer->d_model, layer->d_ff, layer->wdtype);
+    if ((st = check_ws(p, batch, ws, ws_bytes)) != PROX_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int* mi = const_cast<int*>(mask_idx);   // read only in list mode
+    int* mc = const_cast<int*>(mask_count);
+    hipError_t e = launch_upgate(upgate_args(p, layer, x, ws, mi, mc, y), layer->wdtype, batch,
+                                 p.ug_blocks, false, s);
+    if (e != hipSuccess) return hip_fail(e, "stage-2 up/gate launch");
+    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, s);
+    if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_proxy_state(const prox_layer* layer, const void* x, int32_t batch, float tau_x,
+                                      float* s_tilde, int32_t* in_count, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  try {
+    g_err.clear();
+    prox_status st = check_layer(layer);
+    if (st != PROX_OK) return st;
+    if ((st = check_batch(batch)) != PROX_OK) return st;
+    if ((st = check_tau(tau_x, "tau_x")) != PROX_OK) return st;
+    if (!x || !s_tilde) return fail(PROX_ERR_INVALID_ARG, "x and s_tilde must be non-NULL");
+    if (!aligned(x, 16) || !aligned(s_tilde, 4) || (in_count && !aligned(in_count, 4)))
+      return fail(PROX_ERR_INVALID_ARG, "x must be 16-byte aligned, outputs 4-byte aligned");
+    const Plan p = make_plan(layer->d_model, layer->d_ff, layer->wdtype);
+    if ((st = check_ws(p, batch, ws, ws_bytes)) != PROX_OK) return st;
+    hipError_t e = launch_stage1(stage1_args(p, layer, x, tau_x, INFINITY, ws, s_tilde, in_count),
+                                 layer->wdtype, batch, true, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}

@@ -1,0 +1,76 @@
+// Device-side helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prox {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+// Weight / activation element types.  bf16 values travel as raw 16-bit
+// patterns; fp32 as float.
+struct Bf16Tag { typedef uint16_t storage; };
+struct F32Tag { typedef float storage; };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <typename T> __device__ __forceinline__ float load_elem(const void* p, size_t i);
+template <> __device__ __forceinline__ float load_elem<Bf16Tag>(const void* p, size_t i) {
+  return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+template <> __device__ __forceinline__ float load_elem<F32Tag>(const void* p, size_t i) {
+  return static_cast<const float*>(p)[i];
+}
+
+// 16-byte global load.
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Two bf16 pairs multiplied and added into an fp32 accumulator
+// (v_dot2c_f32_bf16: products exact, fp32 sum).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Dot product of 16 bytes of weights with 16 bytes of x (same element type).
+template <typename T> __device__ __forceinline__ float dot16(uint4 w, uint4 x, float acc);
+template <> __device__ __forceinline__ float dot16<Bf16Tag>(uint4 w, uint4 x, float acc) {
+  acc = dot2_bf16(w.x, x.x, acc);
+  acc = dot2_bf16(w.y, x.y, acc);
+  acc = dot2_bf16(w.z, x.z, acc);
+  acc = dot2_bf16(w.w, x.w, acc);
+  return acc;
+}
+template <> __device__ __forceinline__ float dot16<F32Tag>(uint4 w, uint4 x, float acc) {
+  acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+  acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+  acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+  acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
+  return acc;
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// SiLU(z) = z / (1 + e^{-z}); e^{-z} overflowing to +inf gives -0 as required.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace prox

@@ -1,0 +1,95 @@
+// Internal declarations shared by the host library and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/prox.h"
+
+namespace prox {
+
+// ---------------------------------------------------------------------------
+// Kernel geometry (compile-time)
+// ---------------------------------------------------------------------------
+constexpr int kThreads = 256;          // every kernel uses 4 waves of 64
+constexpr int kPanel = 128;            // Stage-1 output columns per block
+constexpr int kLanesPerRow = kPanel / 16;           // 16 columns (16 B) per lane
+constexpr int kRowSlots = kThreads / kLanesPerRow;  // rows in flight per block
+constexpr int kStage1Unroll = 8;       // proxy rows loaded per lane per batch
+constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads)
+constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
+
+// ---------------------------------------------------------------------------
+// Per-launch plan (host-computed, passed by value to kernels)
+// ---------------------------------------------------------------------------
+struct Plan {
+  int d, f, wdtype;
+  // Stage 1
+  int n_panels;      // f / kPanel
+  int splits;        // K-splits over input rows
+  int rows_per_split;
+  // Stage 2 up/gate
+  int ug_blocks;     // blocks per token
+  int ug_max_cpb;    // max channels per block
+  // Stage 2 down
+  int dn_col_slices; // ceil(d / column-slice width)
+  int dn_row_groups;
+  int dn_max_rows;   // max rows per group
+  // workspace layout, bytes per token and offsets inside a token's slice
+  size_t tok_bytes;
+  size_t off_tickets, off_kcount, off_partial, off_bitmap, off_ssp;
+};
+
+Plan make_plan(int d, int f, int wdtype);
+
+struct Stage1Args {
+  int d, f, splits, rows_per_split, n_panels;
+  const uint8_t* proxy_q;
+  const float* proxy_scale;
+  const void* x;          // [batch][d]
+  float tau_x, tau_s;
+  uint8_t* ws;            // base of token 0's slice
+  size_t tok_bytes, off_tickets, off_kcount, off_partial, off_bitmap;
+  float* s_tilde;         // [batch][f] or nullptr
+  int* in_count;          // [batch] or nullptr
+};
+
+struct UpGateArgs {
+  int d, f, max_cpb;
+  const void* w_upgate_t; // [f][2][d]
+  const void* x;          // [batch][d]
+  const uint8_t* ws;      // bitmap source (decode mode)
+  uint8_t* ws_mut;        // s_sp destination
+  size_t tok_bytes, off_bitmap, off_ssp;
+  int* mask_idx;          // decode mode: written; list mode: read (const)
+  int* mask_count;        // decode mode: written; list mode: read
+  float* y;               // zeroed here
+};
+
+struct DownArgs {
+  int d, f, col_slices, row_groups, max_rows;
+  const void* w_down;     // [f][d]
+  const uint8_t* ws;      // s_sp
+  size_t tok_bytes, off_ssp;
+  const int* mask_idx;
+  const int* mask_count;
+  float* y;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_state,
+                         hipStream_t s);
+hipError_t launch_upgate(const UpGateArgs& a, int wdtype, int batch, int blocks,
+                         bool from_bitmap, hipStream_t s);
+hipError_t launch_down(const DownArgs& a, int wdtype, int batch, hipStream_t s);
+hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int wdtype,
+                       uint8_t* proxy_q, float* proxy_scale, void* w_upgate_t, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Calibration helpers: histogram of 8-bit digits of |v| keys that match a
+// prefix; keys are fp32 bit patterns of |value| (values in wdtype or fp32).
+hipError_t launch_digit_histogram(const void* v, size_t n, int vdtype, uint32_t prefix,
+                                  uint32_t prefix_mask, int shift, uint32_t* hist,
+                                  hipStream_t s);
+
+}  // namespace prox

@@ -1,0 +1,244 @@
+// Stage 1 of the Prox decode step on gfx950: input-sparse INT4 proxy and the
+// shared intermediate-channel mask.
+//
+// Method ([blog] = deep-dive blog "Prox 完全拆解", section "Stage 1"):
+//   m_x = 1[|x_i| >= tau_x];  u~ = Pi^in(x, W~_up, m_x);
+//   h~ = SiLU(Pi^in(x, W~_gate, m_x));  s~ = u~ * h~;  m_s = 1[|s~_j| >= tau_s].
+// The pages' kernel ([blog] section on turning the formulas into GPU work) is
+// a fused split-N kernel that shares one read of the hidden state between
+// the up and gate proxies, skips rejected inputs inside the main loop, unpacks
+// INT4 in registers and reduces in FP32, forming s~ and the mask directly.
+//
+// gfx950 design:
+//   * grid = (panels x K-splits, batch).  A panel is 128 output columns; a
+//     K-split is a contiguous range of input rows.  Every block first
+//     compacts the kept rows of its range (ballot + block prefix, ascending)
+//     into LDS together with a = x_i * scale_i for both proxies.
+//   * main loop: 8 lanes cover one kept row's 128-byte slice (16 up + 16 gate
+//     codes per lane, one 16-B load); 32 rows are in flight per block per
+//     step and each lane keeps 8 loads outstanding.  Rejected rows are never
+//     touched, so the bytes read are k_x * 128 per panel.
+//   * INT4 unpack: a nibble masked into the low 10 bits of a half word is an
+//     f16 subnormal equal to nibble * 2^-24 (or 16 * nibble * 2^-24 for the
+//     high nibble of a byte).  v_fma_mix_f32 widens it exactly and fuses the
+//     multiply-add with a * 2^24 (or a * 2^20) in fp32: five bit operations
+//     and eight FMAs per eight codes.  Codes are stored as code + 8, so the
+//     row sums are corrected by 8 * sum(a) once per block.
+//   * the K-split partial sums go to the workspace; a self-resetting ticket
+//     per panel lets the last block add them in fixed split order (so masks
+//     are run-to-run identical), apply SiLU, ballot |s~| >= tau_s and write
+//     the panel's 128 mask bits.
+#include "prox_device.h"
+#include "prox_internal.h"
+
+namespace prox {
+namespace {
+
+struct KeptRow {
+  int row;
+  float a_up;
+  float a_gate;
+};
+
+constexpr int kRedStride = kThreads + 1;  // LDS row of the cross-slot reduction
+
+// Adds the 8 proxy columns packed in one dword (byte b: column 2b in the low
+// nibble, 2b+1 in the high nibble; nibble = code + 8) times `a`, where
+// a24 = a * 2^24 and a20 = a * 2^20 (exact power-of-two scalings).
+__device__ __forceinline__ void acc_dword(float* acc, uint32_t w, float a24, float a20) {
+  const uint32_t t = w >> 8;
+  const f16x2_t h0 = __builtin_bit_cast(f16x2_t, w & 0x000F000Fu);  // cols 0 | 4
+  const f16x2_t h1 = __builtin_bit_cast(f16x2_t, w & 0x00F000F0u);  // cols 1 | 5
+  const f16x2_t h2 = __builtin_bit_cast(f16x2_t, t & 0x000F000Fu);  // cols 2 | 6
+  const f16x2_t h3 = __builtin_bit_cast(f16x2_t, t & 0x00F000F0u);  // cols 3 | 7
+  acc[0] = fmaf(a24, static_cast<float>(h0.x), acc[0]);
+  acc[4] = fmaf(a24, static_cast<float>(h0.y), acc[4]);
+  acc[1] = fmaf(a20, static_cast<float>(h1.x), acc[1]);
+  acc[5] = fmaf(a20, static_cast<float>(h1.y), acc[5]);
+  acc[2] = fmaf(a24, static_cast<float>(h2.x), acc[2]);
+  acc[6] = fmaf(a24, static_cast<float>(h2.y), acc[6]);
+  acc[3] = fmaf(a20, static_cast<float>(h3.x), acc[3]);
+  acc[7] = fmaf(a20, static_cast<float>(h3.y), acc[7]);
+}
+
+template <typename T, bool kWriteState>
+__global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_wave_cnt[4];
+  __shared__ float s_wave_a[2][4];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int b = blockIdx.y;
+  const int panel = blockIdx.x / a.splits;
+  const int split = blockIdx.x - panel * a.splits;
+  const int d = a.d;
+  const int f = a.f;
+  uint8_t* tws = a.ws + static_cast<size_t>(b) * a.tok_bytes;
+  unsigned* tickets = reinterpret_cast<unsigned*>(tws + a.off_tickets);
+  int* kcount = reinterpret_cast<int*>(tws + a.off_kcount);
+  float* partial = reinterpret_cast<float*>(tws + a.off_partial);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(tws + a.off_bitmap);
+
+  // ---- compaction of the kept input rows of this split (ascending order)
+  KeptRow* kept = reinterpret_cast<KeptRow*>(smem);
+  const int row0 = split * a.rows_per_split;
+  const int row1 = min(d, row0 + a.rows_per_split);
+  int nkept = 0;
+  float sum_up = 0.f, sum_gate = 0.f;
+  for (int base = row0; base < row1; base += kThreads) {
+    const int i = base + tid;
+    bool keep = false;
+    float au = 0.f, ag = 0.f;
+    if (i < row1) {
+      const float xv = load_elem<T>(a.x, static_cast<size_t>(b) * d + i);
+      if (fabsf(xv) >= a.tau_x) {
+        keep = true;
+        au = xv * a.proxy_scale[i];
+        ag = xv * a.proxy_scale[d + i];
+      }
+    }
+    const uint64_t bal = __ballot(keep);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = nkept;
+    for (int w2 = 0; w2 < wave; ++w2) off += s_wave_cnt[w2];
+    if (keep) kept[off + below] = KeptRow{i, au, ag};
+    nkept += s_wave_cnt[0] + s_wave_cnt[1] + s_wave_cnt[2] + s_wave_cnt[3];
+    sum_up += au;
+    sum_gate += ag;
+    __syncthreads();
+  }
+  sum_up = wave_sum(sum_up);
+  sum_gate = wave_sum(sum_gate);
+  if (lane == 0) {
+    s_wave_a[0][wave] = sum_up;
+    s_wave_a[1][wave] = sum_gate;
+  }
+
+  // ---- main loop over kept rows: 8 lanes per row, 32 row slots
+  const int slot = tid / kLanesPerRow;
+  const int chunk = tid % kLanesPerRow;
+  const uint8_t* pbase = a.proxy_q + static_cast<size_t>(panel) * kPanel + chunk * 16;
+  float acc_u[16], acc_g[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    acc_u[e] = 0.f;
+    acc_g[e] = 0.f;
+  }
+  constexpr float k2p24 = 16777216.0f;
+  constexpr float k2p20 = 1048576.0f;
+  for (int r0 = slot; r0 < nkept; r0 += kRowSlots * kStage1Unroll) {
+    uint4 w[kStage1Unroll];
+    float au[kStage1Unroll], ag[kStage1Unroll];
+#pragma unroll
+    for (int u = 0; u < kStage1Unroll; ++u) {
+      const int r = r0 + u * kRowSlots;
+      if (r < nkept) {
+        const KeptRow kr = kept[r];
+        w[u] = ldg16(pbase + static_cast<size_t>(kr.row) * f);
+        au[u] = kr.a_up;
+        ag[u] = kr.a_gate;
+      } else {
+        w[u] = make_uint4(0u, 0u, 0u, 0u);
+        au[u] = 0.f;
+        ag[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStage1Unroll; ++u) {
+      const float u24 = au[u] * k2p24, u20 = au[u] * k2p20;
+      const float g24 = ag[u] * k2p24, g20 = ag[u] * k2p20;
+      acc_dword(acc_u + 0, w[u].x, u24, u20);
+      acc_dword(acc_u + 8, w[u].y, u24, u20);
+      acc_dword(acc_g + 0, w[u].z, g24, g20);
+      acc_dword(acc_g + 8, w[u].w, g24, g20);
+    }
+  }
+
+  // ---- reduce the 32 row slots (LDS, fixed order); kept[] is dead now
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    red[e * kRedStride + tid] = acc_u[e];
+    red[(16 + e) * kRedStride + tid] = acc_g[e];
+  }
+  __syncthreads();
+  const int m = tid >> 7;        // 0 = up, 1 = gate
+  const int c = tid & (kPanel - 1);
+  const int ch = c >> 4;
+  const int e = c & 15;
+  float v = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < kRowSlots; ++s) v += red[(m * 16 + e) * kRedStride + s * kLanesPerRow + ch];
+  const float suma = (s_wave_a[m][0] + s_wave_a[m][1]) + (s_wave_a[m][2] + s_wave_a[m][3]);
+  v = fmaf(-8.0f, suma, v);
+  const size_t col = static_cast<size_t>(panel) * kPanel + c;
+  partial[(static_cast<size_t>(split) * 2 + m) * f + col] = v;
+  if (panel == 0 && tid == 0) kcount[split] = nkept;
+
+  // ---- last block of this panel: fixed-order sum of the splits, SiLU, mask
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = atomicAdd(&tickets[panel], 1u);
+    s_last = (prev == static_cast<unsigned>(a.splits - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  float tot = 0.f;
+  for (int k = 0; k < a.splits; ++k)
+    tot += __builtin_nontemporal_load(&partial[(static_cast<size_t>(k) * 2 + m) * f + col]);
+  float* sv = red;  // every thread finished reading red before the ticket barrier
+  sv[tid] = tot;
+  __syncthreads();
+  if (tid < kPanel) {
+    const float uu = sv[tid];
+    const float gg = sv[kPanel + tid];
+    const float st = uu * silu_f32(gg);
+    if (kWriteState) a.s_tilde[static_cast<size_t>(b) * f + col] = st;
+    const uint64_t bal = __ballot(fabsf(st) >= a.tau_s);
+    if (lane == 0) {
+      bitmap[panel * (kPanel / 32) + wave * 2] = static_cast<uint32_t>(bal);
+      bitmap[panel * (kPanel / 32) + wave * 2 + 1] = static_cast<uint32_t>(bal >> 32);
+    }
+  }
+  if (tid == 0) {
+    tickets[panel] = 0u;  // ready for the next stream-ordered call
+    if (panel == 0 && a.in_count != nullptr) {
+      int t = 0;
+      for (int k = 0; k < a.splits; ++k) t += __builtin_nontemporal_load(&kcount[k]);
+      a.in_count[b] = t;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_state,
+                         hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.n_panels * a.splits), static_cast<unsigned>(batch));
+  const size_t kept_bytes = static_cast<size_t>(a.rows_per_split) * sizeof(KeptRow);
+  const size_t red_bytes = static_cast<size_t>(32) * kRedStride * sizeof(float);
+  const size_t smem = kept_bytes > red_bytes ? kept_bytes : red_bytes;
+  if (wdtype == PROX_BF16) {
+    if (write_state)
+      hipLaunchKernelGGL((stage1_kernel<Bf16Tag, true>), grid, dim3(kThreads), smem, s, a);
+    else
+      hipLaunchKernelGGL((stage1_kernel<Bf16Tag, false>), grid, dim3(kThreads), smem, s, a);
+  } else {
+    if (write_state)
+      hipLaunchKernelGGL((stage1_kernel<F32Tag, true>), grid, dim3(kThreads), smem, s, a);
+    else
+      hipLaunchKernelGGL((stage1_kernel<F32Tag, false>), grid, dim3(kThreads), smem, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace prox

@@ -1,0 +1,128 @@
+// Stage 2, second half, on gfx950: the input-sparse down projection.
+//
+// Method ([blog] = deep-dive blog "Prox 完全拆解", sections on the SwiGLU
+// weighted-sum view and "Stage 2"): y = Pi^in(s_sp, W_down, m_s), i.e.
+// y = sum over kept j of s_j * W_down[j, :]; the same index j is an up/gate
+// output channel and a down input row, so only kept rows of W_down are read.
+//
+// gfx950 design:
+//   * W_down is row-major [f][d]: a kept channel is one contiguous d-long run.
+//   * grid = (column slices x row groups, batch).  A column slice is what one
+//     wave covers with one 16-B load per lane (512 bf16 / 256 fp32 columns);
+//     a row group is a contiguous range of the ascending kept list.  The block
+//     stages its (index, s_j) pairs in LDS; each of its 4 waves streams every
+//     4th row with 8 loads in flight and accumulates its columns in registers.
+//   * the 4 waves' partial rows are summed through LDS and the block adds its
+//     slice into y with fp32 atomics (y was zeroed by the up/gate kernel).
+#include "prox_device.h"
+#include "prox_internal.h"
+
+namespace prox {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void axpy16(float* acc, float s, uint4 w);
+
+template <>
+__device__ __forceinline__ void axpy16<Bf16Tag>(float* acc, float s, uint4 w) {
+  acc[0] = fmaf(s, bf16lo(w.x), acc[0]);
+  acc[1] = fmaf(s, bf16hi(w.x), acc[1]);
+  acc[2] = fmaf(s, bf16lo(w.y), acc[2]);
+  acc[3] = fmaf(s, bf16hi(w.y), acc[3]);
+  acc[4] = fmaf(s, bf16lo(w.z), acc[4]);
+  acc[5] = fmaf(s, bf16hi(w.z), acc[5]);
+  acc[6] = fmaf(s, bf16lo(w.w), acc[6]);
+  acc[7] = fmaf(s, bf16hi(w.w), acc[7]);
+}
+
+template <>
+__device__ __forceinline__ void axpy16<F32Tag>(float* acc, float s, uint4 w) {
+  acc[0] = fmaf(s, __uint_as_float(w.x), acc[0]);
+  acc[1] = fmaf(s, __uint_as_float(w.y), acc[1]);
+  acc[2] = fmaf(s, __uint_as_float(w.z), acc[2]);
+  acc[3] = fmaf(s, __uint_as_float(w.w), acc[3]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void down_kernel(DownArgs a) {
+  typedef typename T::storage S;
+  constexpr int kEpl = 16 / sizeof(S);
+  constexpr int kCw = 64 * kEpl;  // columns per slice
+  extern __shared__ __align__(16) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int b = blockIdx.y;
+  const int d = a.d;
+  const int f = a.f;
+  const int cs = blockIdx.x % a.col_slices;
+  const int rg = blockIdx.x / a.col_slices;
+  const int ks = min(max(a.mask_count[b], 0), f);
+  const int per = (ks + a.row_groups - 1) / a.row_groups;
+  const int r0 = min(ks, rg * per);
+  const int r1 = min(ks, r0 + per);
+  const int n = r1 - r0;
+  if (n <= 0) return;  // block-uniform
+
+  float* red = reinterpret_cast<float*>(smem);                 // [4][kCw]
+  int* jr = reinterpret_cast<int*>(red + 4 * kCw);             // [max_rows]
+  float* sr = reinterpret_cast<float*>(jr + a.max_rows);       // [max_rows]
+  const float* ssp = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(b) * a.tok_bytes +
+                                                    a.off_ssp);
+  for (int i = tid; i < n; i += kThreads) {
+    const int j = a.mask_idx[static_cast<size_t>(b) * f + r0 + i];
+    const bool ok = j >= 0 && j < f;
+    jr[i] = ok ? j : -1;
+    sr[i] = ok ? ssp[r0 + i] : 0.f;
+  }
+  __syncthreads();
+
+  const int col = cs * kCw + lane * kEpl;
+  const bool cvalid = col < d;
+  const S* Wd = static_cast<const S*>(a.w_down);
+  float acc[kEpl];
+#pragma unroll
+  for (int e = 0; e < kEpl; ++e) acc[e] = 0.f;
+  for (int i0 = wave; i0 < n; i0 += 4 * kDownUnroll) {
+    uint4 w[kDownUnroll];
+    float sv[kDownUnroll];
+#pragma unroll
+    for (int u = 0; u < kDownUnroll; ++u) {
+      const int i = i0 + u * 4;
+      const int j = i < n ? jr[i] : -1;
+      sv[u] = j >= 0 ? sr[i] : 0.f;
+      if (j >= 0 && cvalid)
+        w[u] = ldg16(Wd + static_cast<size_t>(j) * d + col);
+      else
+        w[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kDownUnroll; ++u) axpy16<T>(acc, sv[u], w[u]);
+  }
+#pragma unroll
+  for (int e = 0; e < kEpl; ++e) red[wave * kCw + lane * kEpl + e] = acc[e];
+  __syncthreads();
+  for (int c = tid; c < kCw; c += kThreads) {
+    const int gc = cs * kCw + c;
+    if (gc < d) {
+      const float v = (red[c] + red[kCw + c]) + (red[2 * kCw + c] + red[3 * kCw + c]);
+      unsafeAtomicAdd(&a.y[static_cast<size_t>(b) * d + gc], v);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_down(const DownArgs& a, int wdtype, int batch, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.col_slices * a.row_groups), static_cast<unsigned>(batch));
+  const int cw = wdtype == PROX_BF16 ? 512 : 256;
+  const size_t smem = static_cast<size_t>(4) * cw * 4 + static_cast<size_t>(a.max_rows) * 8;
+  if (wdtype == PROX_BF16)
+    hipLaunchKernelGGL((down_kernel<Bf16Tag>), grid, dim3(kThreads), smem, s, a);
+  else
+    hipLaunchKernelGGL((down_kernel<F32Tag>), grid, dim3(kThreads), smem, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace prox

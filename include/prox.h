@@ -1,0 +1,207 @@
+/*
+ * prox.h - C ABI of the Prox two-stage sparse SwiGLU FFN decode library
+ * (MI355X / gfx950, HIP).
+ *
+ * The method (sources cited by page and section):
+ *   [blog]  "Prox 完全拆解：先用便宜代理找通道，再用精确计算守住 SwiGLU 的质量"
+ *           (deep-dive blog post on Prox)
+ *   [paper] "Prox: 通过近似中间通道显著性实现 LLM 中免训练的 FFN 激活稀疏化"
+ *           (Chinese rendering of arXiv 2607.27591)
+ *
+ *   Stage 1 ([blog] "Stage 1"): keep the input coordinates with
+ *     |x_i| >= tau_x, run an INT4 proxy of W_up and W_gate over those rows
+ *     only, form the proxy state s~ = u~ * SiLU(g~) and keep the intermediate
+ *     channels with |s~_j| >= tau_s (one mask shared by all three projections).
+ *   Stage 2 ([blog] "Stage 2"): with the dense x and the original weights,
+ *     compute u_j, g_j for the kept channels only, s_j = u_j * SiLU(g_j), and
+ *     y = sum over kept j of s_j * W_down[j, :].
+ *   Pi^in / Pi^out and I(m) are as defined in [paper] section 2.2.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" are HIP device memory; "host" are host memory.
+ *     The caller owns every buffer; the library never allocates or frees
+ *     device memory on the decode path and keeps no pointer after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it unless a function says it blocks.
+ *   - Arguments are validated before anything is enqueued.  On a validation
+ *     failure nothing is enqueued and PROX_ERR_INVALID_ARG or
+ *     PROX_ERR_UNSUPPORTED is returned.  A failed kernel launch returns
+ *     PROX_ERR_HIP.  The message of the last failure on the calling thread is
+ *     available from prox_last_error().  No C++ exception crosses the ABI and
+ *     the library never aborts the process.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Shapes: d_model % 64 == 0, d_ff % 128 == 0, 64 <= d_model <= 12288,
+ *     128 <= d_ff <= 65536 (bounds that keep every block within 64 KB of LDS).  Device pointers to weights, x and y must be
+ *     16-byte aligned; workspaces 256-byte aligned.
+ *   - Weight dtype: PROX_F32 or PROX_BF16 (bf16 bit patterns, RNE).  x uses
+ *     the weight dtype; y and all accumulation are fp32.
+ *   - Thresholds: tau >= 0 or +inf; NaN or negative values are rejected.
+ *     tau = 0 keeps everything; +inf keeps nothing.
+ *   - Concurrent calls must use distinct workspaces.
+ */
+#ifndef PROX_H
+#define PROX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PROX_ABI_VERSION 1
+
+typedef enum {
+  PROX_OK = 0,
+  PROX_ERR_INVALID_ARG = -1,
+  PROX_ERR_UNSUPPORTED = -2,
+  PROX_ERR_HIP = -3,
+  PROX_ERR_INTERNAL = -4
+} prox_status;
+
+typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
+
+/*
+ * One packed FFN layer.  A plain descriptor of caller-owned device buffers;
+ * sizes come from prox_layer_sizes().
+ *
+ * proxy_q     [d_model][d_ff] bytes.  Row i holds the INT4 proxy codes of
+ *             input coordinate i for both W_up and W_gate, so a kept input
+ *             coordinate selects one contiguous d_ff-byte run.  Within a row,
+ *             each group of 16 output columns c0..c0+15 takes 16 bytes:
+ *             8 bytes of up codes, then 8 bytes of gate codes.  In each 8-byte
+ *             half, byte b holds column c0+2b in its low nibble and column
+ *             c0+2b+1 in its high nibble.  A nibble stores code + 8 (offset
+ *             binary), codes are in [-7, 7]; nibble value 0 is never written.
+ * proxy_scale [2][d_model] fp32: per-row scales of the up (0) and gate (1)
+ *             proxies.  Proxy weight = scale[row] * code.
+ * w_upgate_t  [d_ff][2][d_model] in wdtype: for channel j, W_up[:, j] then
+ *             W_gate[:, j], each a contiguous d_model-long run.
+ * w_down      [d_ff][d_model] in wdtype, row-major (row j = W_down[j, :]).
+ */
+typedef struct {
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t wdtype;   /* prox_dtype */
+  int32_t reserved; /* must be 0 */
+  void* proxy_q;
+  float* proxy_scale;
+  void* w_upgate_t;
+  void* w_down;
+} prox_layer;
+
+/* Version of this ABI (PROX_ABI_VERSION). */
+int32_t prox_abi_version(void);
+
+/* Message of the last failure on the calling thread ("" if none).  The
+ * returned pointer stays valid until the next library call on that thread. */
+const char* prox_last_error(void);
+
+/* Byte sizes of the four layer buffers, in prox_layer order:
+ * bytes_out[0] = proxy_q, [1] = proxy_scale, [2] = w_upgate_t, [3] = w_down.
+ * bytes_out is host memory of 4 size_t. */
+prox_status prox_layer_sizes(int32_t d_model, int32_t d_ff, int32_t wdtype, size_t* bytes_out);
+
+/* Workspace bytes needed by prox_ffn_decode / prox_ffn_stage2 /
+ * prox_proxy_state for `batch` tokens (1 <= batch <= 256). */
+prox_status prox_workspace_size(int32_t d_model, int32_t d_ff, int32_t batch, size_t* bytes);
+
+/* Workspace bytes needed by prox_calibrate for n_tokens calibration tokens. */
+prox_status prox_calibrate_workspace_size(int32_t d_model, int32_t d_ff, int32_t n_tokens,
+                                          size_t* bytes);
+
+/* Zero a workspace (device, ws_bytes) on `stream`.  A decode workspace must be
+ * zeroed once before its first use (this call or any zero fill); every
+ * completed call leaves it ready for the next one. */
+prox_status prox_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Offline packing ([blog] "Stage 1": symmetric per-row INT4 proxies of W_up
+ * and W_gate, resident on the GPU; W_down has no proxy).
+ *   W_up, W_gate  device [d_model][d_ff] in wdtype (paper orientation, y = x W)
+ *   W_down        device [d_ff][d_model] in wdtype
+ *   out           host descriptor whose device buffers receive the layout above
+ * Per row r of each proxy matrix: a = max_j |W[r, j]|; scale = fp32(a / 7)
+ * (IEEE division); code = clamp(rint_half_even(fp32(W[r, j] / scale)), -7, 7);
+ * a zero row has scale 0 and codes 0.  W_down is copied unless out->w_down
+ * already equals W_down.  Asynchronous.  Inputs and outputs must not overlap
+ * (except the W_down identity case).
+ */
+prox_status prox_pack_proxy(const void* W_up, const void* W_gate, const void* W_down,
+                            const prox_layer* out, void* stream);
+
+/*
+ * Offline calibration of the two per-layer scalar thresholds ([blog] evidence
+ * section, calibration paragraph: fixed per-layer thresholds from activation
+ * samples).
+ *   X_cal       device [n_tokens][d_model] in wdtype, 1 <= n_tokens <= 65536
+ *   keep_x      fraction of pooled |x| values kept, in [0, 1]
+ *   sparsity_s  fraction of pooled proxy-state magnitudes dropped, in [0, 1]
+ *   tau_x,tau_s HOST outputs
+ *   ws          device, >= prox_calibrate_workspace_size bytes (no zeroing needed)
+ * tau_x is the n-th largest |x| with n = ceil(keep_x * N), N = n_tokens*d_model
+ * (evaluated in double); tau_s is the n-th largest |s~| over all tokens with
+ * n = ceil((1 - (double)sparsity_s) * n_tokens * d_ff), s~ being the Stage-1
+ * proxy state under tau_x.  n = 0 gives +inf.  BLOCKS until done (the call
+ * synchronises `stream`).
+ */
+prox_status prox_calibrate(const prox_layer* layer, const void* X_cal, int32_t n_tokens,
+                           float keep_x, float sparsity_s, float* tau_x, float* tau_s,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step through one FFN layer for `batch` independent tokens
+ * (each token gets its own masks).
+ *   x           device [batch][d_model] in wdtype
+ *   tau_x,tau_s the layer's thresholds
+ *   y           device [batch][d_model] fp32 (overwritten)
+ *   mask_idx    device [batch][d_ff] int32: ascending kept channel indices,
+ *               the first mask_count[b] entries of row b are valid
+ *   mask_count  device [batch] int32 (k_s per token)
+ *   in_count    device [batch] int32 (k_x per token) or NULL
+ *   ws          device, >= prox_workspace_size(batch) bytes, zeroed once
+ * Asynchronous: three kernels on `stream`, no host synchronisation.
+ */
+prox_status prox_ffn_decode(const prox_layer* layer, const void* x, int32_t batch,
+                            float tau_x, float tau_s, float* y, int32_t* mask_idx,
+                            int32_t* mask_count, int32_t* in_count, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * prox_ffn_decode that also records four hipEvent_t (host array `events`,
+ * passed as void*): [0] before Stage 1, [1] after Stage 1, [2] after the
+ * Stage-2 up/gate kernel, [3] after the down kernel.  For timing only.
+ */
+prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32_t batch,
+                                   float tau_x, float tau_s, float* y, int32_t* mask_idx,
+                                   int32_t* mask_count, int32_t* in_count, void* ws,
+                                   size_t ws_bytes, void* stream, void* const* events);
+
+/*
+ * Stage 2 alone ([blog] "Stage 2") from a caller-given channel list.
+ *   mask_idx    device [batch][d_ff] int32, ascending indices in [0, d_ff);
+ *               entries outside that range are skipped
+ *   mask_count  device [batch] int32, clamped to [0, d_ff]
+ *   y           device [batch][d_model] fp32 (overwritten)
+ * Asynchronous.
+ */
+prox_status prox_ffn_stage2(const prox_layer* layer, const void* x, int32_t batch,
+                            const int32_t* mask_idx, const int32_t* mask_count, float* y,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage 1 alone: the proxy state s~ ([blog] "Stage 1", equations for u~, h~,
+ * s~) for every channel.
+ *   s_tilde     device [batch][d_ff] fp32
+ *   in_count    device [batch] int32 or NULL
+ * Asynchronous.
+ */
+prox_status prox_proxy_state(const prox_layer* layer, const void* x, int32_t batch,
+                             float tau_x, float* s_tilde, int32_t* in_count, void* ws,
+                             size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PROX_H */

@@ -119,8 +119,11 @@ def proxy_state(x, q_up, sc_up, q_gate, sc_gate, tau_x):
     """
     x = np.asarray(x, dtype=np.float64)
     m_x = input_mask(x, tau_x)
-    u = pi_in(x, dequantize(q_up, sc_up), m_x)
-    g = pi_in(x, dequantize(q_gate, sc_gate), m_x)
+    idx = index_set(m_x)
+    # Pi^in reads only the rows I(m_x) of W~, so only those rows are
+    # dequantised: W~[I, :] = diag(scale[I]) q[I, :].
+    u = x[idx] @ dequantize(q_up[idx], sc_up[idx])
+    g = x[idx] @ dequantize(q_gate[idx], sc_gate[idx])
     s = u * silu(g)
     return {"u": u, "g": g, "s": s, "m_x": m_x}
 

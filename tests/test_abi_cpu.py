@@ -1,0 +1,122 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol and
+rejects bad arguments before touching a device (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prox.h")
+
+P = pytest.importorskip("free_ffn_activation_amd.prox",
+                        reason="libprox.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(prox_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert "prox_ffn_decode" in names and "prox_pack_proxy" in names and "prox_calibrate" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (prox_[a-z0-9_]+)", out))
+    assert set(names) <= exported, f"missing: {set(names) - exported}"
+    assert set(names) == set(P.EXPORTED)
+    lib = P.raw_library()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_sizes():
+    assert P.prox_abi_version() == 1
+    s = P.prox_layer_sizes(4096, 12288, P.PROX_BF16)
+    assert s == (4096 * 12288, 2 * 4096 * 4, 2 * 12288 * 4096 * 2, 12288 * 4096 * 2)
+    s32 = P.prox_layer_sizes(256, 768, P.PROX_F32)
+    assert s32[2] == 2 * 256 * 768 * 4
+    w1 = P.prox_workspace_size(4096, 12288, 1)
+    assert w1 % 256 == 0 and P.prox_workspace_size(4096, 12288, 8) == 8 * w1
+    assert P.prox_calibrate_workspace_size(4096, 12288, 256) >= 256 * 12288 * 4
+
+
+@pytest.mark.parametrize("d,f,dt,status", [(100, 768, 1, P.PROX_ERR_UNSUPPORTED),
+                                           (256, 700, 1, P.PROX_ERR_UNSUPPORTED),
+                                           (32, 768, 1, P.PROX_ERR_INVALID_ARG),
+                                           (256, 768, 7, P.PROX_ERR_INVALID_ARG),
+                                           (16384, 768, 0, P.PROX_ERR_UNSUPPORTED),
+                                           (4096, 131072, 1, P.PROX_ERR_UNSUPPORTED)])
+def test_bad_shapes(d, f, dt, status):
+    with pytest.raises(P.ProxError) as ei:
+        P.prox_layer_sizes(d, f, dt)
+    assert ei.value.status == status
+    assert P.prox_last_error() != ""
+
+
+FAKE = 1 << 40  # a 256-aligned address that is never dereferenced by validation
+
+
+def _layer(d=256, f=768, dt=0, **kw):
+    L = P.prox_layer(d, f, dt, 0, FAKE, FAKE, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(L, k, v)
+    return L
+
+
+def _decode(L, x=FAKE, batch=1, tx=0.5, ts=0.1, y=FAKE, mi=FAKE, mc=FAKE, ic=None, ws=FAKE,
+            nbytes=1 << 30):
+    lib = P.raw_library()
+    return lib.prox_ffn_decode(ctypes.byref(L) if L is not None else None, x, batch, tx, ts, y, mi,
+                               mc, ic, ws, nbytes, None)
+
+
+def test_decode_argument_validation():
+    ok_layer = _layer()
+    assert _decode(None) == P.PROX_ERR_INVALID_ARG
+    assert _decode(_layer(proxy_q=None)) == P.PROX_ERR_INVALID_ARG
+    assert _decode(_layer(reserved=1)) == P.PROX_ERR_INVALID_ARG
+    assert _decode(_layer(d=250)) == P.PROX_ERR_UNSUPPORTED
+    assert _decode(_layer(w_down=FAKE + 8)) == P.PROX_ERR_INVALID_ARG     # misaligned
+    assert _decode(ok_layer, batch=0) == P.PROX_ERR_INVALID_ARG
+    assert _decode(ok_layer, batch=257) == P.PROX_ERR_INVALID_ARG
+    assert _decode(ok_layer, tx=math.nan) == P.PROX_ERR_INVALID_ARG
+    assert _decode(ok_layer, ts=-1.0) == P.PROX_ERR_INVALID_ARG
+    assert _decode(ok_layer, x=None) == P.PROX_ERR_INVALID_ARG
+    assert _decode(ok_layer, y=FAKE + 4) == P.PROX_ERR_INVALID_ARG
+    assert _decode(ok_layer, ws=None) == P.PROX_ERR_INVALID_ARG
+    assert _decode(ok_layer, ws=FAKE + 16) == P.PROX_ERR_INVALID_ARG
+    need = P.prox_workspace_size(256, 768, 2)
+    assert _decode(ok_layer, batch=2, nbytes=need - 1) == P.PROX_ERR_INVALID_ARG
+    assert "workspace" in P.prox_last_error()
+
+
+def test_other_entry_points_validate():
+    lib = P.raw_library()
+    L = _layer()
+    tx, ts = ctypes.c_float(), ctypes.c_float()
+    # calibrate: fractions outside [0, 1], tokens out of range, small workspace
+    assert lib.prox_calibrate(ctypes.byref(L), FAKE, 64, 1.5, 0.7, ctypes.byref(tx),
+                              ctypes.byref(ts), FAKE, 1 << 30, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_calibrate(ctypes.byref(L), FAKE, 0, 0.5, 0.7, ctypes.byref(tx),
+                              ctypes.byref(ts), FAKE, 1 << 30, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_calibrate(ctypes.byref(L), FAKE, 64, 0.5, 0.7, ctypes.byref(tx),
+                              ctypes.byref(ts), FAKE, 16, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_calibrate(ctypes.byref(L), FAKE, 64, 0.5, 0.7, None, ctypes.byref(ts),
+                              FAKE, 1 << 30, None) == P.PROX_ERR_INVALID_ARG
+    # pack: NULL / misaligned inputs
+    assert lib.prox_pack_proxy(None, FAKE, FAKE, ctypes.byref(L), None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_pack_proxy(FAKE + 2, FAKE, FAKE, ctypes.byref(L), None) == P.PROX_ERR_INVALID_ARG
+    # stage 2 / proxy state
+    assert lib.prox_ffn_stage2(ctypes.byref(L), FAKE, 1, None, FAKE, FAKE, FAKE, 1 << 30,
+                               None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_proxy_state(ctypes.byref(L), FAKE, 1, math.nan, FAKE, None, FAKE, 1 << 30,
+                                None) == P.PROX_ERR_INVALID_ARG
+    # events variant needs the event array
+    assert lib.prox_ffn_decode_events(ctypes.byref(L), FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE, None,
+                                      FAKE, 1 << 30, None, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_workspace_init(None, 16, None) == P.PROX_ERR_INVALID_ARG

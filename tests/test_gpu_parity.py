@@ -1,0 +1,296 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Comparison rules: packed codes, scales, input masks and counts bit-exact;
+channel masks bit-exact outside a 1e-3 relative band around tau_s (in-band
+disagreements are counted and printed); y within max-abs 2e-2 and relative
+L2 1e-2 of the oracle, computed from the same channel list.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from prox_gpu_util import (band_compare, decode_proxy_bytes, oracle_layer, oracle_view,
+                           pack_layer, to_device, y_errors, y_ok)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from free_ffn_activation_amd import prox
+    return prox
+
+
+def _small_cfg(d, f, dtype, seed, std=0.05, batch=1):
+    return synth.LayerConfig(f"s{d}x{f}", d, f, dtype, std, max(1, d // 64), 20.0, 16, 0.5, 0.7,
+                             batch, seed)
+
+
+def _bufs(P, L, b):
+    dev = "cuda"
+    return (torch.empty(b, L.d_model, dtype=torch.float32, device=dev),
+            torch.empty(b, L.d_ff, dtype=torch.int32, device=dev),
+            torch.empty(b, dtype=torch.int32, device=dev),
+            torch.empty(b, dtype=torch.int32, device=dev))
+
+
+def _oracle_taus(ov, keep_x=0.5, sparsity_s=0.7, n_tok=None):
+    xc = ov["x_cal"] if n_tok is None else ov["x_cal"][:n_tok]
+    return oracle.calibrate(xc, ov["qu"], ov["su"], ov["qg"], ov["sg"], keep_x, sparsity_s)
+
+
+def _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, label):
+    dt = layer.cfg.dtype
+    x = to_device(layer.x_dec[tokens], dt)
+    b = len(tokens)
+    y, mi, mc, ic = _bufs(P, L, b)
+    ws = P.new_workspace(L.d_model, L.d_ff, b)
+    P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, ws)
+    torch.cuda.synchronize()
+    y, mi, mc, ic = y.cpu().numpy(), mi.cpu().numpy(), mc.cpu().numpy(), ic.cpu().numpy()
+    total_band = 0
+    for k, t in enumerate(tokens):
+        ref = oracle.decode(ov["x_dec"][t], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"],
+                            ov["qg"], ov["sg"], tau_x, tau_s)
+        assert ic[k] == ref["k_x"], f"{label} token {t}: k_x {ic[k]} != {ref['k_x']}"
+        oob, inb, asc = band_compare(mi[k], int(mc[k]), ref["s_tilde"], tau_s)
+        assert asc, f"{label} token {t}: index list not ascending / in range"
+        assert oob == 0, f"{label} token {t}: {oob} channel(s) outside the band disagree"
+        total_band += inb
+        # y against the oracle's Stage 2 on the GPU's own channel list
+        m_gpu = np.zeros(L.d_ff, bool)
+        m_gpu[mi[k][: mc[k]]] = True
+        y_ref = oracle.stage2(ov["x_dec"][t], ov["Wu"], ov["Wg"], ov["Wd"], m_gpu)["y"]
+        if not m_gpu.any():
+            assert np.all(y[k] == 0.0)
+        else:
+            ma, rl = y_errors(y[k], y_ref)
+            assert y_ok(y[k], y_ref), f"{label} token {t}: y max-abs {ma:.3e} rel-L2 {rl:.3e}"
+    print(f"[{label}] tokens={list(tokens)} k_s={list(mc)} k_x={list(ic)} in-band={total_band}")
+    return y, mi, mc, ic
+
+
+# ------------------------------------------------------------------ packing
+@pytest.mark.parametrize("name,d,f,dtype", [("tiny", 256, 768, "f32"),
+                                            ("bf16-small", 320, 384, "bf16"),
+                                            ("qwen3_8b", 4096, 12288, "bf16")])
+def test_pack_bit_exact(P, name, d, f, dtype):
+    if name in synth.CONFIGS:
+        layer, ov = oracle_layer(name)
+    else:
+        layer = synth.make_layer(_small_cfg(d, f, dtype, 31))
+        ov = oracle_view(layer)
+    L = pack_layer(layer)
+    q = L.proxy_q.cpu().numpy()
+    up, gate, nib_ok = decode_proxy_bytes(q, d, f)
+    assert nib_ok, "a nibble of 0 was written"
+    assert np.array_equal(up, ov["qu"].astype(np.int16))
+    assert np.array_equal(gate, ov["qg"].astype(np.int16))
+    sc = L.proxy_scale.cpu().numpy()
+    assert np.array_equal(sc[:d].view(np.uint32), ov["su"].view(np.uint32))
+    assert np.array_equal(sc[d:].view(np.uint32), ov["sg"].view(np.uint32))
+    wt = L.w_upgate_t.cpu().numpy().reshape(f, 2, d)
+    wd = L.w_down.cpu().numpy().reshape(f, d)
+    src_u = layer.w_up.view(np.int16) if dtype == "bf16" else layer.w_up
+    src_g = layer.w_gate.view(np.int16) if dtype == "bf16" else layer.w_gate
+    src_d = layer.w_down.view(np.int16) if dtype == "bf16" else layer.w_down
+    assert np.array_equal(wt[:, 0, :], src_u.T)
+    assert np.array_equal(wt[:, 1, :], src_g.T)
+    assert np.array_equal(wd, src_d)
+
+
+def test_pack_ties_and_zero_rows(P):
+    d, f = 64, 128
+    W = np.zeros((d, f), dtype=np.float32)
+    W[1, :4] = np.array([7.0, 3.5, 2.5, -3.5]) * 2.0 ** -6
+    W[2, :4] = np.array([-7.0, 0.5, -0.5, 1.5]) * 2.0 ** -3
+    rng = np.random.default_rng(0)
+    W[3:] = rng.standard_normal((d - 3, f)).astype(np.float32)
+    Wd = rng.standard_normal((f, d)).astype(np.float32)
+    L = P.ProxLayer(d, f, P.PROX_F32)
+    P.prox_pack_proxy(to_device(W, "f32"), to_device(-W, "f32"), to_device(Wd, "f32"), L)
+    torch.cuda.synchronize()
+    up, gate, _ = decode_proxy_bytes(L.proxy_q.cpu().numpy(), d, f)
+    qu, su = oracle.pack_proxy(W.astype(np.float64))
+    qg, sg = oracle.pack_proxy(-W.astype(np.float64))
+    assert np.array_equal(up, qu) and np.array_equal(gate, qg)
+    assert list(up[1, :4]) == [7, 4, 2, -4] and np.all(up[0] == 0)
+    sc = L.proxy_scale.cpu().numpy()
+    assert sc[0] == 0 and np.array_equal(sc[:d], su) and np.array_equal(sc[d:], sg)
+
+
+# ------------------------------------------------------------------ stage 1
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b"])
+def test_proxy_state_and_input_mask(P, name):
+    layer, ov = oracle_layer(name)
+    L = pack_layer(layer)
+    cfg = layer.cfg
+    tau_x = float(np.float32(np.median(np.abs(ov["x_cal"]))))
+    tokens = [0, 1, 2]
+    x = to_device(layer.x_dec[tokens], cfg.dtype)
+    st = torch.empty(len(tokens), cfg.d_ff, dtype=torch.float32, device="cuda")
+    ic = torch.empty(len(tokens), dtype=torch.int32, device="cuda")
+    ws = P.new_workspace(cfg.d_model, cfg.d_ff, len(tokens))
+    P.prox_proxy_state(L, x, tau_x, st, ic, ws)
+    torch.cuda.synchronize()
+    st, ic = st.cpu().numpy(), ic.cpu().numpy()
+    for k, t in enumerate(tokens):
+        ref = oracle.proxy_state(ov["x_dec"][t], ov["qu"], ov["su"], ov["qg"], ov["sg"], tau_x)
+        assert ic[k] == int(ref["m_x"].sum())
+        scale = np.max(np.abs(ref["s"]))
+        err = np.max(np.abs(st[k] - ref["s"]))
+        assert err <= 1e-5 * scale, f"token {t}: s~ error {err:.3e} vs scale {scale:.3e}"
+    # second call on the same workspace: bit-identical (fixed reduction order)
+    st2 = torch.empty(len(tokens), cfg.d_ff, dtype=torch.float32, device="cuda")
+    P.prox_proxy_state(L, x, tau_x, st2, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(st2.cpu().numpy().view(np.uint32), st.view(np.uint32))
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("name,tokens", [("tiny", [0, 1, 2, 3]), ("qwen3_8b", [0, 1])])
+def test_decode_parity(P, name, tokens):
+    layer, ov = oracle_layer(name)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov, n_tok=None if name == "tiny" else 16)
+    for t in tokens:
+        _run_decode(P, L, layer, ov, [t], tau_x, tau_s, f"{name}")
+
+
+def test_decode_batch8_per_token_masks(P):
+    layer, ov = oracle_layer("qwen3_8b_batch8", n_dec=8, n_cal=16)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov)
+    y, mi, mc, ic = _run_decode(P, L, layer, ov, list(range(8)), tau_x, tau_s, "batch8")
+    assert len(set(int(v) for v in mc)) > 1  # masks really are per token
+
+
+def test_decode_qwen3_32b(P):
+    cfg = synth.CONFIGS["qwen3_32b"]
+    layer = synth.make_layer(cfg, n_dec=2, n_cal=8)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov)
+    _run_decode(P, L, layer, ov, [0], tau_x, tau_s, "qwen3_32b")
+
+
+def test_decode_ragged_small_shapes(P):
+    """Shapes off the large power-of-two grid: partial column slices (d = 320),
+    few panels (f = 384), minimum sizes (64 x 128), bf16 and fp32."""
+    for (d, f, dt, seed) in [(320, 384, "bf16", 41), (64, 128, "f32", 42), (576, 1152, "bf16", 43),
+                             (192, 640, "f32", 44)]:
+        layer = synth.make_layer(_small_cfg(d, f, dt, seed), n_dec=3)
+        ov = oracle_view(layer)
+        L = pack_layer(layer)
+        tau_x, tau_s = _oracle_taus(ov)
+        _run_decode(P, L, layer, ov, [0, 1, 2], tau_x, tau_s, f"{d}x{f}-{dt}")
+
+
+def test_decode_degenerate_thresholds(P):
+    layer, ov = oracle_layer("tiny")
+    L = pack_layer(layer)
+    d, f = L.d_model, L.d_ff
+    # all-pass: dense SwiGLU
+    y, mi, mc, ic = _run_decode(P, L, layer, ov, [0], 0.0, 0.0, "all-pass")
+    assert mc[0] == f and ic[0] == d and np.array_equal(mi[0], np.arange(f))
+    # no input kept and tau_s > 0: empty channel mask, y = 0
+    y, mi, mc, ic = _run_decode(P, L, layer, ov, [1], math.inf, 1e-6, "no-input")
+    assert ic[0] == 0 and mc[0] == 0 and np.all(y == 0)
+    # no input kept but tau_s = 0: every channel, exact dense Stage 2
+    y, mi, mc, ic = _run_decode(P, L, layer, ov, [1], math.inf, 0.0, "no-input-all-channels")
+    assert mc[0] == f
+    # tau_s = +inf: empty channel mask
+    y, mi, mc, ic = _run_decode(P, L, layer, ov, [2], 0.0, math.inf, "empty")
+    assert mc[0] == 0 and np.all(y == 0)
+
+
+def test_decode_repeatable_masks(P):
+    layer, ov = oracle_layer("qwen3_8b")
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov, n_tok=16)
+    x = to_device(layer.x_dec[[3]], "bf16")
+    ws = P.new_workspace(L.d_model, L.d_ff, 1)
+    outs = []
+    for _ in range(3):
+        y, mi, mc, ic = _bufs(P, L, 1)
+        P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, ws)
+        torch.cuda.synchronize()
+        outs.append((y.cpu().numpy(), mi.cpu().numpy(), int(mc.item())))
+    for y, mi, mc in outs[1:]:
+        assert mc == outs[0][2] and np.array_equal(mi[0, :mc], outs[0][1][0, :mc])
+        ma, rl = y_errors(y[0], outs[0][0][0].astype(np.float64))
+        assert rl < 1e-6
+
+
+# ------------------------------------------------------------------ stage 2 alone
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b"])
+def test_stage2_from_oracle_mask(P, name):
+    layer, ov = oracle_layer(name)
+    L = pack_layer(layer)
+    cfg = layer.cfg
+    tau_x, tau_s = _oracle_taus(ov, n_tok=None if name == "tiny" else 16)
+    tokens = [4, 5]
+    b = len(tokens)
+    J = np.zeros((b, cfg.d_ff), dtype=np.int32)
+    cnt = np.zeros(b, dtype=np.int32)
+    refs = []
+    for k, t in enumerate(tokens):
+        ref = oracle.decode(ov["x_dec"][t], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"],
+                            ov["qg"], ov["sg"], tau_x, tau_s)
+        cnt[k] = ref["k_s"]
+        J[k, : ref["k_s"]] = ref["J"]
+        refs.append(ref)
+    x = to_device(layer.x_dec[tokens], cfg.dtype)
+    y = torch.empty(b, cfg.d_model, dtype=torch.float32, device="cuda")
+    ws = P.new_workspace(cfg.d_model, cfg.d_ff, b)
+    P.prox_ffn_stage2(L, x, torch.from_numpy(J).cuda(), torch.from_numpy(cnt).cuda(), y, ws)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    for k in range(b):
+        ma, rl = y_errors(y[k], refs[k]["y"])
+        print(f"[stage2 {name}] token {tokens[k]} k_s={cnt[k]} max-abs={ma:.3e} rel-L2={rl:.3e}")
+        assert y_ok(y[k], refs[k]["y"])
+
+
+def test_stage2_skips_out_of_range_indices(P):
+    layer, ov = oracle_layer("tiny")
+    L = pack_layer(layer)
+    f = L.d_ff
+    J = np.array([[3, -5, 17, f + 9, 40] + [0] * (f - 5)], dtype=np.int32)
+    cnt = np.array([5], dtype=np.int32)
+    x = to_device(layer.x_dec[[0]], "f32")
+    y = torch.empty(1, L.d_model, dtype=torch.float32, device="cuda")
+    ws = P.new_workspace(L.d_model, f, 1)
+    P.prox_ffn_stage2(L, x, torch.from_numpy(J).cuda(), torch.from_numpy(cnt).cuda(), y, ws)
+    torch.cuda.synchronize()
+    m = np.zeros(f, bool)
+    m[[3, 17, 40]] = True
+    y_ref = oracle.stage2(ov["x_dec"][0], ov["Wu"], ov["Wg"], ov["Wd"], m)["y"]
+    assert y_ok(y.cpu().numpy()[0], y_ref)
+
+
+# ------------------------------------------------------------------ calibration
+@pytest.mark.parametrize("name,n_tok", [("tiny", 64), ("qwen3_8b", 16)])
+def test_calibrate_parity(P, name, n_tok):
+    layer, ov = oracle_layer(name)
+    L = pack_layer(layer)
+    cfg = layer.cfg
+    xc = to_device(layer.x_cal[:n_tok], cfg.dtype)
+    ws = torch.empty(P.prox_calibrate_workspace_size(cfg.d_model, cfg.d_ff, n_tok),
+                     dtype=torch.uint8, device="cuda")
+    tx, ts = P.prox_calibrate(L, xc, cfg.keep_x, cfg.sparsity_s, ws)
+    rx, rs = _oracle_taus(ov, cfg.keep_x, cfg.sparsity_s, n_tok=n_tok)
+    print(f"[calibrate {name}] tau_x gpu={tx!r} oracle={rx!r}  tau_s gpu={ts!r} oracle={rs!r}")
+    assert np.float32(tx) == np.float32(rx)
+    assert abs(ts - rs) <= 1e-5 * rs
+    # edge fractions: keep everything / nothing
+    tx0, ts0 = P.prox_calibrate(L, xc, 1.0, 0.0, ws)
+    assert tx0 == float(np.min(np.abs(ov["x_cal"][:n_tok]))) and ts0 >= 0.0
+    tx1, ts1 = P.prox_calibrate(L, xc, 0.0, 1.0, ws)
+    assert math.isinf(tx1) and math.isinf(ts1)
