@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the Prox sparse SwiGLU FFN decode step on one MI355X.
+
+Metric: microseconds per FFN layer, plus achieved HBM GB/s and the fraction of
+the 8 TB/s roofline on the bytes the method must move, at 70% intermediate
+sparsity and 50% input keep, batch 1, on a Qwen3-8B-shaped layer
+(d_model 4096, d_ff 12288, bf16 weights, fp32 accumulation).
+
+Method of measurement
+  * 8 independent seeded layers (2.8 GB of packed weights) are rotated so the
+    256 MB Infinity Cache cannot hold the working set; each step decodes one
+    seeded Laplace token through one layer (prox_ffn_decode: three kernels).
+  * The headline number times K steps replayed from a HIP graph (the per-step
+    GPU work is ~20 us, shorter than eager host launch overhead); the eager
+    rate is reported beside it.
+  * A second pass records HIP events around each kernel (on the stream the
+    kernels run on) to give per-kernel durations; the dominant kernel's
+    algorithmic bytes over its mean duration is the roofline figure.
+  * Required bytes per step use the actual k_x and k_s of each token:
+    k_x*d_ff (INT4 up+gate rows) + 8*k_x (scales) + 3*k_s*d_model*2 (kept bf16
+    rows of W_up^T, W_gate^T, W_down) + 2*d_model (x) + 4*d_model (y) + 4*k_s.
+  * Dense comparators on the same rotation: torch bf16 (one fused up/gate
+    GEMV, SiLU, product, down GEMV) and this library's Stage-2 kernels with
+    every channel kept.
+  * CPU baseline: the plain NumPy oracle on the host cores, on a bounded
+    sample of tokens of layer 0.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, os.path.join(ROOT, "tests")):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+METRIC = "µs per FFN layer + achieved HBM GB/s (% roofline) at 70% sparsity, batch 1"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1280)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="qwen3_8b", choices=["qwen3_8b", "qwen3_32b", "stack36"])
+    ap.add_argument("--layers", type=int, default=None, help="layer instances rotated")
+    ap.add_argument("--sparsity", type=float, default=0.7)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        sys.exit(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+                 "(the decode path has no multi-GPU mode)")
+
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import synth
+    from free_ffn_activation_amd import prox
+    from prox_gpu_util import pack_layer, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg_name = {"qwen3_8b": "qwen3_8b", "qwen3_32b": "qwen3_32b", "stack36": "qwen3_8b_stack"}[args.workload]
+    cfg = synth.CONFIGS[cfg_name]
+    n_layers = args.layers or {"qwen3_8b": 8, "qwen3_32b": 4, "stack36": 36}[args.workload]
+    d, f = cfg.d_model, cfg.d_ff
+    n_tok = 16
+    sparsity = args.sparsity
+
+    # ---------------------------------------------------------------- layers
+    log(f"generating {n_layers} seeded {cfg.name} layers (d={d}, f={f})")
+    t0 = time.time()
+    with ThreadPoolExecutor(8) as ex:
+        host_layers = list(ex.map(lambda i: synth.make_layer(cfg, i, n_dec=n_tok), range(n_layers)))
+    log(f"generated in {time.time() - t0:.1f}s; packing + calibrating on the GPU")
+    layers, taus = [], []
+    cal_ws = torch.empty(prox.prox_calibrate_workspace_size(d, f, cfg.n_cal), dtype=torch.uint8,
+                         device=dev)
+    x_all = torch.empty(n_layers, n_tok, d, dtype=torch.int16, device=dev)
+    for i, hl in enumerate(host_layers):
+        L = pack_layer(hl)
+        xc = to_device(hl.x_cal, cfg.dtype)
+        taus.append(prox.prox_calibrate(L, xc, cfg.keep_x, sparsity, cal_ws))
+        x_all[i].copy_(to_device(hl.x_dec, cfg.dtype))
+        layers.append(L)
+        del xc
+    layer0_host = host_layers[0]
+    del host_layers
+    del cal_ws
+    torch.cuda.synchronize()
+    log(f"packed {n_layers} layers ({sum(L.nbytes for L in layers) / 1e9:.2f} GB resident)")
+
+    # ---------------------------------------------------------------- schedule
+    steps_per_round = n_layers * n_tok
+    sched = [(s % n_layers, (s // n_layers) % n_tok) for s in range(steps_per_round)]
+    y = torch.empty(1, d, dtype=torch.float32, device=dev)
+    mi = torch.empty(1, f, dtype=torch.int32, device=dev)
+    mc = torch.empty(1, dtype=torch.int32, device=dev)
+    ic = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = prox.new_workspace(d, f, 1)
+    xs = [[x_all[l, t:t + 1] for t in range(n_tok)] for l in range(n_layers)]
+
+    def step(s):
+        l, t = sched[s % steps_per_round]
+        tx, ts = taus[l]
+        prox.prox_ffn_decode(layers[l], xs[l][t], tx, ts, y, mi, mc, ic, ws)
+
+    # counts per (layer, token): deterministic, recorded once
+    kx = np.zeros((n_layers, n_tok), np.int64)
+    ksv = np.zeros((n_layers, n_tok), np.int64)
+    for l in range(n_layers):
+        for t in range(n_tok):
+            tx, ts = taus[l]
+            prox.prox_ffn_decode(layers[l], xs[l][t], tx, ts, y, mi, mc, ic, ws)
+            torch.cuda.synchronize()
+            kx[l, t], ksv[l, t] = int(ic.item()), int(mc.item())
+    w = 2
+    breq = kx * f + 8 * kx + 3 * ksv * d * w + d * w + 4 * d + 4 * ksv
+    by_stage1 = kx * f + 8 * kx + d * w + f // 8
+    by_upgate = 2 * ksv * d * w + d * w + f // 8 + 8 * ksv
+    by_down = ksv * d * w + 8 * ksv + 4 * d
+    log(f"mean k_x={kx.mean():.1f} ({kx.mean() / d:.3f} of d), mean k_s={ksv.mean():.1f} "
+        f"({ksv.mean() / f:.3f} of f), mean required bytes {breq.mean() / 1e6:.2f} MB")
+
+    def sched_mean(a):
+        return float(np.mean([a[l, t] for (l, t) in sched]))
+
+    K = max(1, args.steps)
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- eager timing
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(s)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) / K * 1e6
+    log(f"eager: {eager_us:.2f} us/layer")
+
+    # ---------------------------------------------------------------- graph timing
+    def time_graph(fn, label):
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for s in range(steps_per_round):  # warm the capture stream
+                fn(s)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for s in range(steps_per_round):
+                fn(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, int(math.ceil(K / steps_per_round)))
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        ev0.record()
+        for _ in range(reps):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        us = ev0.elapsed_time(ev1) * 1e3 / (reps * steps_per_round)
+        log(f"{label}: {us:.2f} us/layer over {reps * steps_per_round} graph-replayed steps "
+            f"(wall {wall * 1e3:.1f} ms)")
+        del g
+        return us, reps * steps_per_round, wall
+
+    if args.no_graph:
+        prox_us, timed_steps, wall = eager_us, K, None
+    else:
+        prox_us, timed_steps, wall = time_graph(step, "prox graph")
+
+    # ---------------------------------------------------------------- per-kernel events
+    n_ev = min(steps_per_round, 256)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(100_000_000)  # keep the GPU busy while the host enqueues
+    for s in range(n_ev):
+        l, t = sched[s]
+        tx, ts = taus[l]
+        prox.prox_ffn_decode_events(layers[l], xs[l][t], tx, ts, y, mi, mc, ic, ws, evs[s])
+    torch.cuda.synchronize()
+    k_us = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for i in range(3)]
+                     for s in range(n_ev)])
+    k_mean = k_us.mean(axis=0)
+    step_ev_us = np.array([evs[s][0].elapsed_time(evs[s][3]) * 1e3 for s in range(n_ev)])
+    log("kernel split (us, mean): stage1 %.2f  upgate %.2f  down %.2f  (event-bracketed step %.2f)"
+        % (k_mean[0], k_mean[1], k_mean[2], step_ev_us.mean()))
+    sub = sched[:n_ev]
+    bytes_k = [float(np.mean([a[l, t] for (l, t) in sub])) for a in (by_stage1, by_upgate, by_down)]
+    names = ["stage1_proxy", "stage2_upgate", "stage2_down"]
+    dom = int(np.argmax(k_mean))
+    ach = bytes_k[dom] / (k_mean[dom] * 1e-6) / 1e9
+    kernels = {names[i]: {"us": round(float(k_mean[i]), 3),
+                          "algorithmic_MB": round(bytes_k[i] / 1e6, 3),
+                          "GBps": round(bytes_k[i] / (k_mean[i] * 1e-6) / 1e9, 1)}
+               for i in range(3)}
+
+    # ---------------------------------------------------------------- dense comparators
+    dense = {}
+    if not args.no_dense:
+        wug = [L.w_upgate_t.view(torch.bfloat16).view(2 * f, d) for L in layers]
+        wdn = [L.w_down.view(torch.bfloat16).view(f, d) for L in layers]
+        xb = [[xs[l][t].view(torch.bfloat16) for t in range(n_tok)] for l in range(n_layers)]
+        yb = torch.empty(1, d, dtype=torch.bfloat16, device=dev)
+
+        def dense_torch(s):
+            l, t = sched[s % steps_per_round]
+            ug = torch.nn.functional.linear(xb[l][t], wug[l])
+            sv = ug[:, 0::2] * torch.nn.functional.silu(ug[:, 1::2])
+            torch.matmul(sv, wdn[l], out=yb)
+
+        all_j = torch.arange(f, dtype=torch.int32, device=dev).view(1, f)
+        all_c = torch.full((1,), f, dtype=torch.int32, device=dev)
+
+        def dense_own(s):
+            l, t = sched[s % steps_per_round]
+            prox.prox_ffn_stage2(layers[l], xs[l][t], all_j, all_c, y, ws)
+
+        for fn, label in ((dense_torch, "dense_torch_bf16"), (dense_own, "dense_own_stage2")):
+            for s in range(8):
+                fn(s)
+            torch.cuda.synchronize()
+            dense[label] = round(time_graph(fn, label)[0], 3) if not args.no_graph else None
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        import threadpoolctl
+        from prox_gpu_util import oracle_view
+        log("CPU oracle baseline: preparing layer 0 in fp64")
+        ov = oracle_view(layer0_host)
+        tx, ts = taus[0]
+        times = []
+        t_start = time.perf_counter()
+        tok = 0
+        while (time.perf_counter() - t_start < args.cpu_seconds and tok < n_tok) or tok < 2:
+            t1 = time.perf_counter()
+            oracle.decode(ov["x_dec"][tok], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"],
+                          ov["qg"], ov["sg"], tx, ts)
+            times.append(time.perf_counter() - t1)
+            tok += 1
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        cpu = {"value": round(statistics.mean(times) * 1e6, 1), "unit": "us/layer",
+               "cores": int(threads), "kind": "oracle",
+               "sample": f"{len(times)} decode tokens of layer 0 ({cfg.name}, d={d}, f={f}), "
+                         f"NumPy fp64 oracle, {sum(times):.1f} s of CPU work"}
+        log(f"CPU oracle: {cpu['value']:.0f} us/layer on {threads} threads ({len(times)} tokens)")
+
+    mean_breq = sched_mean(breq)
+    gbps = mean_breq / (prox_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(prox_us, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": timed_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prox_us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}_ffn_layer_decode", "d_model": d, "d_ff": f,
+                   "batch": 1, "keep_x": cfg.keep_x, "sparsity_s": sparsity,
+                   "layers_rotated": n_layers, "tokens_per_layer": n_tok,
+                   "timing": "eager" if args.no_graph else "hip_graph_replay"},
+        "achieved_GBps": round(gbps, 1),
+        "pct_hbm_roofline": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "required_MB_per_layer": round(mean_breq / 1e6, 3),
+        "mean_k_x": round(sched_mean(kx), 1),
+        "mean_k_s": round(sched_mean(ksv), 1),
+        "eager_us_per_layer": round(eager_us, 3),
+        "kernels": kernels,
+        "dense_us_per_layer": dense,
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

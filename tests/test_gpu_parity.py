@@ -294,3 +294,53 @@ def test_calibrate_parity(P, name, n_tok):
     assert tx0 == float(np.min(np.abs(ov["x_cal"][:n_tok]))) and ts0 >= 0.0
     tx1, ts1 = P.prox_calibrate(L, xc, 0.0, 1.0, ws)
     assert math.isinf(tx1) and math.isinf(ts1)
+
+
+# ------------------------------------------------------------------ graph replay
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b"])
+def test_graph_replay_matches_eager(P, name):
+    """prox_ffn_decode captured in a HIP graph: every replay (with eager work and
+    synchronisations in between) reproduces the eager masks and y."""
+    layer, ov = oracle_layer(name)
+    L = pack_layer(layer)
+    cfg = layer.cfg
+    tau_x, tau_s = _oracle_taus(ov, n_tok=None if name == "tiny" else 16)
+    toks = [0, 1, 2]
+    xs = [to_device(layer.x_dec[[t]], cfg.dtype) for t in toks]
+    ws = P.new_workspace(cfg.d_model, cfg.d_ff, 1)
+    outs = [_bufs(P, L, 1) for _ in toks]
+    eager = []
+    for x in xs:
+        y, mi, mc, ic = _bufs(P, L, 1)
+        P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, ws)
+        torch.cuda.synchronize()
+        eager.append((y.cpu().numpy(), mi.cpu().numpy(), int(mc.item()), int(ic.item())))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for x, (y, mi, mc, ic) in zip(xs, outs):
+            P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for x, (y, mi, mc, ic) in zip(xs, outs):
+            P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, ws)
+    for rep in range(4):
+        for (y, mi, mc, ic) in outs:
+            y.fill_(123.0)
+            mc.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (y, mi, mc, ic) in enumerate(outs):
+            ey, emi, emc, eic = eager[k]
+            assert int(mc.item()) == emc and int(ic.item()) == eic, f"replay {rep} token {k}"
+            assert np.array_equal(mi.cpu().numpy()[0, :emc], emi[0, :emc])
+            ma, rl = y_errors(y.cpu().numpy()[0], ey[0].astype(np.float64))
+            assert rl <= 1e-6, f"replay {rep} token {k}: rel {rl:.2e}"
+        # eager work on the same workspace between replays
+        yy, mi2, mc2, ic2 = _bufs(P, L, 1)
+        P.prox_ffn_decode(L, xs[rep % len(xs)], tau_x, tau_s, yy, mi2, mc2, ic2, ws)
+        torch.cuda.synchronize()
+        assert int(mc2.item()) == eager[rep % len(xs)][2]
+    del g
