@@ -201,6 +201,9 @@ def main() -> int:
     # ---------------------------------------------------------------- per-kernel events
     n_ev = min(steps_per_round, 256)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    for row in evs:  # torch creates the underlying HIP event on first record
+        for ev in row:
+            ev.record()
     torch.cuda.synchronize()
     torch.cuda._sleep(100_000_000)  # keep the GPU busy while the host enqueues
     for s in range(n_ev):

@@ -28,6 +28,15 @@
 //     per panel lets the last block add them in fixed split order (so masks
 //     are run-to-run identical), apply SiLU, ballot |s~| >= tau_s and write
 //     the panel's 128 mask bits.
+//   * hand-off between blocks without cache-wide maintenance: the partials
+//     are written with device-scope stores (sc1: written through to the point
+//     of coherence shared by all XCDs), every thread waits for its stores to
+//     complete (vmcnt 0) before the block barrier, one thread then bumps the
+//     ticket with a device-scope atomic, and the last block reads the
+//     partials with device-scope loads (sc1), issued only after its ticket
+//     returned.  An agent-scope fence would instead write back and invalidate
+//     the whole L2 of the XCD once per wave, which costs far more than the
+//     kernel's own traffic.
 #include "prox_device.h"
 #include "prox_internal.h"
 
@@ -178,23 +187,26 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   const float suma = (s_wave_a[m][0] + s_wave_a[m][1]) + (s_wave_a[m][2] + s_wave_a[m][3]);
   v = fmaf(-8.0f, suma, v);
   const size_t col = static_cast<size_t>(panel) * kPanel + c;
-  partial[(static_cast<size_t>(split) * 2 + m) * f + col] = v;
-  if (panel == 0 && tid == 0) kcount[split] = nkept;
+  __hip_atomic_store(&partial[(static_cast<size_t>(split) * 2 + m) * f + col], v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  if (panel == 0 && tid == 0)
+    __hip_atomic_store(&kcount[split], nkept, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- last block of this panel: fixed-order sum of the splits, SiLU, mask
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are complete
   __syncthreads();
   if (tid == 0) {
-    const unsigned prev = atomicAdd(&tickets[panel], 1u);
+    const unsigned prev =
+        __hip_atomic_fetch_add(&tickets[panel], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == static_cast<unsigned>(a.splits - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   float tot = 0.f;
   for (int k = 0; k < a.splits; ++k)
-    tot += __builtin_nontemporal_load(&partial[(static_cast<size_t>(k) * 2 + m) * f + col]);
+    tot += __hip_atomic_load(&partial[(static_cast<size_t>(k) * 2 + m) * f + col], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   float* sv = red;  // every thread finished reading red before the ticket barrier
   sv[tid] = tot;
   __syncthreads();
@@ -210,10 +222,12 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     }
   }
   if (tid == 0) {
-    tickets[panel] = 0u;  // ready for the next stream-ordered call
+    // ready for the next stream-ordered call
+    __hip_atomic_store(&tickets[panel], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (panel == 0 && a.in_count != nullptr) {
       int t = 0;
-      for (int k = 0; k < a.splits; ++k) t += __builtin_nontemporal_load(&kcount[k]);
+      for (int k = 0; k < a.splits; ++k)
+        t += __hip_atomic_load(&kcount[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       a.in_count[b] = t;
     }
   }
