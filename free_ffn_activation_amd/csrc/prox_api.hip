@@ -265,11 +265,16 @@ Plan make_plan(int d, int f, int wdtype) {
   // up/gate: enough 4-wave blocks for one kept channel per wave at ~30% keep
   p.ug_blocks = std::max(64, f / 12);
   p.ug_max_cpb = (f + p.ug_blocks - 1) / p.ug_blocks;
-  // down: column slices of one wave-load, row groups to reach ~768 blocks
+  // down: column slices of one wave-load, row groups to reach ~256 blocks of
+  // 16 waves (few blocks keep the number of y atomics low)
   const int cw = 64 * (16 / static_cast<int>(elem_size(wdtype)));
   p.dn_col_slices = (d + cw - 1) / cw;
-  int rg = static_cast<int>(std::lround(768.0 / p.dn_col_slices));
-  rg = std::max(1, std::min(f / 4, rg));
+  int rg = static_cast<int>(std::lround(256.0 / p.dn_col_slices));
+  rg = std::max(1, std::min(f / 16, rg));
+  // LDS per block: the 16 waves' partial rows plus (index, s) per row of the group
+  const int red_bytes = (kDownThreads / 64) * cw * 4;
+  const int max_rows_cap = (61440 - red_bytes) / 8;
+  rg = std::max(rg, (f + max_rows_cap - 1) / max_rows_cap);
   p.dn_row_groups = rg;
   p.dn_max_rows = (f + rg - 1) / rg;
   // per-token workspace slice

@@ -19,6 +19,7 @@ constexpr int kRowSlots = kThreads / kLanesPerRow;  // rows in flight per block
 constexpr int kStage1Unroll = 8;       // proxy rows loaded per lane per batch
 constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads)
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
+constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column slice
 
 // ---------------------------------------------------------------------------
 // Per-launch plan (host-computed, passed by value to kernels)

@@ -16,7 +16,8 @@
 //     into LDS together with a = x_i * scale_i for both proxies.
 //   * main loop: 8 lanes cover one kept row's 128-byte slice (16 up + 16 gate
 //     codes per lane, one 16-B load); 32 rows are in flight per block per
-//     step and each lane keeps 8 loads outstanding.  Rejected rows are never
+//     step and each lane keeps 8 loads outstanding; x and the two scales of
+//     a row are fetched in one round trip.  Rejected rows are never
 //     touched, so the bytes read are k_x * 128 per panel.
 //   * INT4 unpack: a nibble masked into the low 10 bits of a half word is an
 //     f16 subnormal equal to nibble * 2^-24 (or 16 * nibble * 2^-24 for the
@@ -99,16 +100,14 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   float sum_up = 0.f, sum_gate = 0.f;
   for (int base = row0; base < row1; base += kThreads) {
     const int i = base + tid;
-    bool keep = false;
-    float au = 0.f, ag = 0.f;
-    if (i < row1) {
-      const float xv = load_elem<T>(a.x, static_cast<size_t>(b) * d + i);
-      if (fabsf(xv) >= a.tau_x) {
-        keep = true;
-        au = xv * a.proxy_scale[i];
-        ag = xv * a.proxy_scale[d + i];
-      }
-    }
+    // x and both scales are fetched together (one memory round trip)
+    const int ii = min(i, row1 - 1);
+    const float xv = load_elem<T>(a.x, static_cast<size_t>(b) * d + ii);
+    const float sc_up = a.proxy_scale[ii];
+    const float sc_gate = a.proxy_scale[d + ii];
+    const bool keep = i < row1 && fabsf(xv) >= a.tau_x;
+    const float au = keep ? xv * sc_up : 0.f;
+    const float ag = keep ? xv * sc_gate : 0.f;
     const uint64_t bal = __ballot(keep);
     const int below = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
@@ -140,22 +139,18 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   }
   constexpr float k2p24 = 16777216.0f;
   constexpr float k2p20 = 1048576.0f;
+  // Loads are unconditional (a slot past the end re-reads the last kept row
+  // with weight 0) so the compiler can wait on them one at a time.
   for (int r0 = slot; r0 < nkept; r0 += kRowSlots * kStage1Unroll) {
     uint4 w[kStage1Unroll];
     float au[kStage1Unroll], ag[kStage1Unroll];
 #pragma unroll
     for (int u = 0; u < kStage1Unroll; ++u) {
       const int r = r0 + u * kRowSlots;
-      if (r < nkept) {
-        const KeptRow kr = kept[r];
-        w[u] = ldg16(pbase + static_cast<size_t>(kr.row) * f);
-        au[u] = kr.a_up;
-        ag[u] = kr.a_gate;
-      } else {
-        w[u] = make_uint4(0u, 0u, 0u, 0u);
-        au[u] = 0.f;
-        ag[u] = 0.f;
-      }
+      const KeptRow kr = kept[min(r, nkept - 1)];
+      w[u] = ldg16(pbase + static_cast<size_t>(kr.row) * f);
+      au[u] = r < nkept ? kr.a_up : 0.f;
+      ag[u] = r < nkept ? kr.a_gate : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kStage1Unroll; ++u) {
@@ -203,10 +198,21 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   __syncthreads();
   if (!s_last) return;
 
+  // issue the split loads in groups of 8 so they travel together; the sum
+  // keeps the fixed split order
   float tot = 0.f;
-  for (int k = 0; k < a.splits; ++k)
-    tot += __hip_atomic_load(&partial[(static_cast<size_t>(k) * 2 + m) * f + col], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+  for (int k0 = 0; k0 < a.splits; k0 += 8) {
+    float pv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = min(k0 + u, a.splits - 1);
+      pv[u] = __hip_atomic_load(&partial[(static_cast<size_t>(k) * 2 + m) * f + col], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < a.splits) tot += pv[u];
+  }
   float* sv = red;  // every thread finished reading red before the ticket barrier
   sv[tid] = tot;
   __syncthreads();

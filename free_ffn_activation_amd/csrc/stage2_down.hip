@@ -10,10 +10,12 @@
 //   * grid = (column slices x row groups, batch).  A column slice is what one
 //     wave covers with one 16-B load per lane (512 bf16 / 256 fp32 columns);
 //     a row group is a contiguous range of the ascending kept list.  The block
-//     stages its (index, s_j) pairs in LDS; each of its 4 waves streams every
-//     4th row with 8 loads in flight and accumulates its columns in registers.
-//   * the 4 waves' partial rows are summed through LDS and the block adds its
+//     stages its (index, s_j) pairs in LDS; each of its 16 waves streams every
+//     16th row with 8 loads in flight and accumulates its columns in registers.
+//   * the 16 waves' partial rows are summed through LDS and the block adds its
 //     slice into y with fp32 atomics (y was zeroed by the up/gate kernel).
+//     Large blocks keep the atomic count (row groups x d) low: fp32 global
+//     atomics cost far more per byte than the weight stream.
 #include "prox_device.h"
 #include "prox_internal.h"
 
@@ -44,7 +46,7 @@ __device__ __forceinline__ void axpy16<F32Tag>(float* acc, float s, uint4 w) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void down_kernel(DownArgs a) {
+__global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
   typedef typename T::storage S;
   constexpr int kEpl = 16 / sizeof(S);
   constexpr int kCw = 64 * kEpl;  // columns per slice
@@ -65,12 +67,13 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownArgs a) {
   const int n = r1 - r0;
   if (n <= 0) return;  // block-uniform
 
-  float* red = reinterpret_cast<float*>(smem);                 // [4][kCw]
-  int* jr = reinterpret_cast<int*>(red + 4 * kCw);             // [max_rows]
+  constexpr int kWaves = kDownThreads / 64;
+  float* red = reinterpret_cast<float*>(smem);                 // [kWaves][kCw]
+  int* jr = reinterpret_cast<int*>(red + kWaves * kCw);        // [max_rows]
   float* sr = reinterpret_cast<float*>(jr + a.max_rows);       // [max_rows]
   const float* ssp = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(b) * a.tok_bytes +
                                                     a.off_ssp);
-  for (int i = tid; i < n; i += kThreads) {
+  for (int i = tid; i < n; i += kDownThreads) {
     const int j = a.mask_idx[static_cast<size_t>(b) * f + r0 + i];
     const bool ok = j >= 0 && j < f;
     jr[i] = ok ? j : -1;
@@ -84,18 +87,19 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownArgs a) {
   float acc[kEpl];
 #pragma unroll
   for (int e = 0; e < kEpl; ++e) acc[e] = 0.f;
-  for (int i0 = wave; i0 < n; i0 += 4 * kDownUnroll) {
+  // Loads are unconditional: a slot past the end (or a skipped index) re-reads
+  // a valid row with weight 0, and a lane past the last column reads the
+  // slice's first column, so the compiler can wait on the loads one by one.
+  const int colc = cvalid ? col : cs * kCw;
+  for (int i0 = wave; i0 < n; i0 += kWaves * kDownUnroll) {
     uint4 w[kDownUnroll];
     float sv[kDownUnroll];
 #pragma unroll
     for (int u = 0; u < kDownUnroll; ++u) {
-      const int i = i0 + u * 4;
-      const int j = i < n ? jr[i] : -1;
-      sv[u] = j >= 0 ? sr[i] : 0.f;
-      if (j >= 0 && cvalid)
-        w[u] = ldg16(Wd + static_cast<size_t>(j) * d + col);
-      else
-        w[u] = make_uint4(0u, 0u, 0u, 0u);
+      const int i = min(i0 + u * kWaves, n - 1);
+      const int j = jr[i];
+      sv[u] = (i0 + u * kWaves < n && j >= 0 && cvalid) ? sr[i] : 0.f;
+      w[u] = ldg16(Wd + static_cast<size_t>(j >= 0 ? j : 0) * d + colc);
     }
 #pragma unroll
     for (int u = 0; u < kDownUnroll; ++u) axpy16<T>(acc, sv[u], w[u]);
@@ -103,10 +107,12 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownArgs a) {
 #pragma unroll
   for (int e = 0; e < kEpl; ++e) red[wave * kCw + lane * kEpl + e] = acc[e];
   __syncthreads();
-  for (int c = tid; c < kCw; c += kThreads) {
+  for (int c = tid; c < kCw; c += kDownThreads) {
     const int gc = cs * kCw + c;
     if (gc < d) {
-      const float v = (red[c] + red[kCw + c]) + (red[2 * kCw + c] + red[3 * kCw + c]);
+      float v = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2) v += red[w2 * kCw + c];
       unsafeAtomicAdd(&a.y[static_cast<size_t>(b) * d + gc], v);
     }
   }
@@ -117,11 +123,11 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownArgs a) {
 hipError_t launch_down(const DownArgs& a, int wdtype, int batch, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.col_slices * a.row_groups), static_cast<unsigned>(batch));
   const int cw = wdtype == PROX_BF16 ? 512 : 256;
-  const size_t smem = static_cast<size_t>(4) * cw * 4 + static_cast<size_t>(a.max_rows) * 8;
+  const size_t smem = static_cast<size_t>(kDownThreads / 64) * cw * 4 + static_cast<size_t>(a.max_rows) * 8;
   if (wdtype == PROX_BF16)
-    hipLaunchKernelGGL((down_kernel<Bf16Tag>), grid, dim3(kThreads), smem, s, a);
+    hipLaunchKernelGGL((down_kernel<Bf16Tag>), grid, dim3(kDownThreads), smem, s, a);
   else
-    hipLaunchKernelGGL((down_kernel<F32Tag>), grid, dim3(kThreads), smem, s, a);
+    hipLaunchKernelGGL((down_kernel<F32Tag>), grid, dim3(kDownThreads), smem, s, a);
   return hipGetLastError();
 }
 

@@ -134,25 +134,21 @@ __global__ __launch_bounds__(kThreads) void upgate_kernel(UpGateArgs a) {
       const uint4* wg = reinterpret_cast<const uint4*>(W + static_cast<size_t>(j) * 2 * d + d);
       for (int s0 = 0; s0 < nsteps; s0 += kUpGateUnroll) {
         uint4 lu[kUpGateUnroll], lg[kUpGateUnroll];
+        // unconditional loads (clamped to the run) so waits pipeline
 #pragma unroll
         for (int u = 0; u < kUpGateUnroll; ++u) {
-          const int cidx = (s0 + u) * 64 + lane;
-          if (cidx < nchunks) {
-            lu[u] = ldg16(wu + cidx);
-            lg[u] = ldg16(wg + cidx);
-          } else {
-            lu[u] = make_uint4(0u, 0u, 0u, 0u);
-            lg[u] = make_uint4(0u, 0u, 0u, 0u);
-          }
+          const int cidx = min((s0 + u) * 64 + lane, nchunks - 1);
+          lu[u] = ldg16(wu + cidx);
+          lg[u] = ldg16(wg + cidx);
         }
 #pragma unroll
         for (int u = 0; u < kUpGateUnroll; ++u) {
           const int cidx = (s0 + u) * 64 + lane;
-          if (cidx < nchunks) {
-            const uint4 xv = xs[cidx];
-            su = dot16<T>(lu[u], xv, su);
-            sg = dot16<T>(lg[u], xv, sg);
-          }
+          const uint4 xv = xs[min(cidx, nchunks - 1)];
+          const float du = dot16<T>(lu[u], xv, 0.f);
+          const float dg = dot16<T>(lg[u], xv, 0.f);
+          su += cidx < nchunks ? du : 0.f;
+          sg += cidx < nchunks ? dg : 0.f;
         }
       }
       su = wave_sum(su);
