@@ -93,6 +93,7 @@ Stage1Args stage1_args(const Plan& p, const prox_layer* L, const void* x, float 
   a.splits = p.splits;
   a.rows_per_split = p.rows_per_split;
   a.n_panels = p.n_panels;
+  a.panel = p.panel;
   a.proxy_q = static_cast<const uint8_t*>(L->proxy_q);
   a.proxy_scale = L->proxy_scale;
   a.x = x;
@@ -252,7 +253,10 @@ Plan make_plan(int d, int f, int wdtype) {
   p.d = d;
   p.f = f;
   p.wdtype = wdtype;
-  p.n_panels = f / kPanel;
+  // 128-column panels: wider panels gather faster but double the split
+  // partials and the last block's reduction, which costs more than it saves
+  p.panel = 128;
+  p.n_panels = f / p.panel;
   // about three 256-thread blocks per CU over 256 CUs for Stage 1
   const int target = 768;
   int splits = static_cast<int>(std::lround(static_cast<double>(target) / p.n_panels));

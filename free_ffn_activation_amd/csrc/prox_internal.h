@@ -13,9 +13,6 @@ namespace prox {
 // Kernel geometry (compile-time)
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 256;          // every kernel uses 4 waves of 64
-constexpr int kPanel = 128;            // Stage-1 output columns per block
-constexpr int kLanesPerRow = kPanel / 16;           // 16 columns (16 B) per lane
-constexpr int kRowSlots = kThreads / kLanesPerRow;  // rows in flight per block
 constexpr int kStage1Unroll = 8;       // proxy rows loaded per lane per batch
 constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads)
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
@@ -27,7 +24,8 @@ constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column
 struct Plan {
   int d, f, wdtype;
   // Stage 1
-  int n_panels;      // f / kPanel
+  int panel;         // Stage-1 output columns per block (256 or 128)
+  int n_panels;      // f / panel
   int splits;        // K-splits over input rows
   int rows_per_split;
   // Stage 2 up/gate
@@ -45,7 +43,7 @@ struct Plan {
 Plan make_plan(int d, int f, int wdtype);
 
 struct Stage1Args {
-  int d, f, splits, rows_per_split, n_panels;
+  int d, f, splits, rows_per_split, n_panels, panel;
   const uint8_t* proxy_q;
   const float* proxy_scale;
   const void* x;          // [batch][d]

@@ -10,15 +10,18 @@
 // INT4 in registers and reduces in FP32, forming s~ and the mask directly.
 //
 // gfx950 design:
-//   * grid = (panels x K-splits, batch).  A panel is 128 output columns; a
-//     K-split is a contiguous range of input rows.  Every block first
-//     compacts the kept rows of its range (ballot + block prefix, ascending)
-//     into LDS together with a = x_i * scale_i for both proxies.
-//   * main loop: 8 lanes cover one kept row's 128-byte slice (16 up + 16 gate
-//     codes per lane, one 16-B load); 32 rows are in flight per block per
-//     step and each lane keeps 8 loads outstanding; x and the two scales of
-//     a row are fetched in one round trip.  Rejected rows are never
-//     touched, so the bytes read are k_x * 128 per panel.
+//   * grid = (panels x K-splits, batch).  A panel is 128 output columns, a
+//     128-byte run of each kept row (the kernel also builds for 256).  A
+//     K-split is a contiguous range of input rows.  Each wave of a block
+//     compacts the kept rows of a quarter of that range (ballot + popcount,
+//     ascending) into a wave-private LDS list together with a = x_i * scale_i
+//     for both proxies, then gathers those rows; no block barrier precedes
+//     the gather.
+//   * main loop: 8 lanes cover one kept row's 128-byte slice (16 up + 16
+//     gate codes per lane, one 16-B load); each lane keeps 8 loads
+//     outstanding; x and the two scales of a row are fetched in one round
+//     trip.  Rejected rows are never
+//     touched, so the bytes read are k_x * panel width per panel.
 //   * INT4 unpack: a nibble masked into the low 10 bits of a half word is an
 //     f16 subnormal equal to nibble * 2^-24 (or 16 * nibble * 2^-24 for the
 //     high nibble of a byte).  v_fma_mix_f32 widens it exactly and fuses the
@@ -71,8 +74,11 @@ __device__ __forceinline__ void acc_dword(float* acc, uint32_t w, float a24, flo
   acc[7] = fmaf(a20, static_cast<float>(h3.y), acc[7]);
 }
 
-template <typename T, bool kWriteState>
+template <typename T, bool kWriteState, int kPw>
 __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
+  constexpr int kLpr = kPw / 16;             // lanes per row (16 columns each)
+  constexpr int kSlots = kThreads / kLpr;    // row slots per block
+  constexpr int kNout = 2 * kPw / kThreads;  // outputs per thread (up and gate)
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_wave_cnt[4];
   __shared__ float s_wave_a[2][4];
@@ -92,45 +98,48 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   float* partial = reinterpret_cast<float*>(tws + a.off_partial);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(tws + a.off_bitmap);
 
-  // ---- compaction of the kept input rows of this split (ascending order)
-  KeptRow* kept = reinterpret_cast<KeptRow*>(smem);
+  // ---- compaction: each wave takes a quarter of this split's rows and
+  // compacts its kept rows (ascending) into a wave-private LDS list; no block
+  // barrier is needed before the gather starts.
   const int row0 = split * a.rows_per_split;
   const int row1 = min(d, row0 + a.rows_per_split);
+  const int wchunk = (a.rows_per_split + 3) / 4;
+  const int wr0 = min(row1, row0 + wave * wchunk);
+  const int wr1 = min(row1, wr0 + wchunk);
+  KeptRow* kept = reinterpret_cast<KeptRow*>(smem) + wave * wchunk;
   int nkept = 0;
   float sum_up = 0.f, sum_gate = 0.f;
-  for (int base = row0; base < row1; base += kThreads) {
-    const int i = base + tid;
+  for (int base = wr0; base < wr1; base += 64) {
+    const int i = base + lane;
     // x and both scales are fetched together (one memory round trip)
-    const int ii = min(i, row1 - 1);
+    const int ii = min(i, wr1 - 1);
     const float xv = load_elem<T>(a.x, static_cast<size_t>(b) * d + ii);
     const float sc_up = a.proxy_scale[ii];
     const float sc_gate = a.proxy_scale[d + ii];
-    const bool keep = i < row1 && fabsf(xv) >= a.tau_x;
+    const bool keep = i < wr1 && fabsf(xv) >= a.tau_x;
     const float au = keep ? xv * sc_up : 0.f;
     const float ag = keep ? xv * sc_gate : 0.f;
     const uint64_t bal = __ballot(keep);
-    const int below = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = nkept;
-    for (int w2 = 0; w2 < wave; ++w2) off += s_wave_cnt[w2];
-    if (keep) kept[off + below] = KeptRow{i, au, ag};
-    nkept += s_wave_cnt[0] + s_wave_cnt[1] + s_wave_cnt[2] + s_wave_cnt[3];
+    if (keep) kept[nkept + __popcll(bal & ((1ull << lane) - 1ull))] = KeptRow{i, au, ag};
+    nkept += __popcll(bal);
     sum_up += au;
     sum_gate += ag;
-    __syncthreads();
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   sum_up = wave_sum(sum_up);
   sum_gate = wave_sum(sum_gate);
   if (lane == 0) {
     s_wave_a[0][wave] = sum_up;
     s_wave_a[1][wave] = sum_gate;
+    s_wave_cnt[wave] = nkept;
   }
 
-  // ---- main loop over kept rows: 8 lanes per row, 32 row slots
-  const int slot = tid / kLanesPerRow;
-  const int chunk = tid % kLanesPerRow;
-  const uint8_t* pbase = a.proxy_q + static_cast<size_t>(panel) * kPanel + chunk * 16;
+  // ---- main loop over the wave's kept rows: kLpr lanes per row
+  const int wslot = lane / kLpr;
+  const int chunk = lane % kLpr;
+  const uint8_t* pbase = a.proxy_q + static_cast<size_t>(panel) * kPw + chunk * 16;
   float acc_u[16], acc_g[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -139,19 +148,21 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   }
   constexpr float k2p24 = 16777216.0f;
   constexpr float k2p20 = 1048576.0f;
+  constexpr int kWaveSlots = 64 / kLpr;
   // Loads are unconditional (a slot past the end re-reads the last kept row
   // with weight 0) so the compiler can wait on them one at a time.
-  for (int r0 = slot; r0 < nkept; r0 += kRowSlots * kStage1Unroll) {
+  for (int r0 = wslot; r0 < nkept; r0 += kWaveSlots * kStage1Unroll) {
     uint4 w[kStage1Unroll];
     float au[kStage1Unroll], ag[kStage1Unroll];
 #pragma unroll
     for (int u = 0; u < kStage1Unroll; ++u) {
-      const int r = r0 + u * kRowSlots;
+      const int r = r0 + u * kWaveSlots;
       const KeptRow kr = kept[min(r, nkept - 1)];
       w[u] = ldg16(pbase + static_cast<size_t>(kr.row) * f);
       au[u] = r < nkept ? kr.a_up : 0.f;
       ag[u] = r < nkept ? kr.a_gate : 0.f;
     }
+    __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
 #pragma unroll
     for (int u = 0; u < kStage1Unroll; ++u) {
       const float u24 = au[u] * k2p24, u20 = au[u] * k2p20;
@@ -163,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     }
   }
 
-  // ---- reduce the 32 row slots (LDS, fixed order); kept[] is dead now
+  // ---- reduce the row slots (LDS, fixed order); kept[] is dead now
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -172,20 +183,29 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     red[(16 + e) * kRedStride + tid] = acc_g[e];
   }
   __syncthreads();
-  const int m = tid >> 7;        // 0 = up, 1 = gate
-  const int c = tid & (kPanel - 1);
-  const int ch = c >> 4;
-  const int e = c & 15;
-  float v = 0.f;
+  float v[kNout];
+  size_t col[kNout];
+  int mm[kNout];
+#pragma unroll
+  for (int k = 0; k < kNout; ++k) {
+    const int o = tid + k * kThreads;
+    const int m = o / kPw;  // 0 = up, 1 = gate
+    const int c = o % kPw;
+    const int ch = c >> 4;
+    const int e = c & 15;
+    float t = 0.f;
 #pragma unroll 8
-  for (int s = 0; s < kRowSlots; ++s) v += red[(m * 16 + e) * kRedStride + s * kLanesPerRow + ch];
-  const float suma = (s_wave_a[m][0] + s_wave_a[m][1]) + (s_wave_a[m][2] + s_wave_a[m][3]);
-  v = fmaf(-8.0f, suma, v);
-  const size_t col = static_cast<size_t>(panel) * kPanel + c;
-  __hip_atomic_store(&partial[(static_cast<size_t>(split) * 2 + m) * f + col], v, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+    for (int sl = 0; sl < kSlots; ++sl) t += red[(m * 16 + e) * kRedStride + sl * kLpr + ch];
+    const float suma = (s_wave_a[m][0] + s_wave_a[m][1]) + (s_wave_a[m][2] + s_wave_a[m][3]);
+    v[k] = fmaf(-8.0f, suma, t);
+    col[k] = static_cast<size_t>(panel) * kPw + c;
+    mm[k] = m;
+    __hip_atomic_store(&partial[(static_cast<size_t>(split) * 2 + m) * f + col[k]], v[k],
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (panel == 0 && tid == 0)
-    __hip_atomic_store(&kcount[split], nkept, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&kcount[split], s_wave_cnt[0] + s_wave_cnt[1] + s_wave_cnt[2] + s_wave_cnt[3],
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- last block of this panel: fixed-order sum of the splits, SiLU, mask
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are complete
@@ -198,33 +218,38 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   __syncthreads();
   if (!s_last) return;
 
-  // issue the split loads in groups of 8 so they travel together; the sum
-  // keeps the fixed split order
-  float tot = 0.f;
-  for (int k0 = 0; k0 < a.splits; k0 += 8) {
-    float pv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = min(k0 + u, a.splits - 1);
-      pv[u] = __hip_atomic_load(&partial[(static_cast<size_t>(k) * 2 + m) * f + col], __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (k0 + u < a.splits) tot += pv[u];
-  }
+  // split loads go out in groups of 8 so they travel together; the sums keep
+  // the fixed split order
   float* sv = red;  // every thread finished reading red before the ticket barrier
-  sv[tid] = tot;
+#pragma unroll
+  for (int k = 0; k < kNout; ++k) {
+    float tot = 0.f;
+    for (int k0 = 0; k0 < a.splits; k0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int kk = min(k0 + u, a.splits - 1);
+        pv[u] = __hip_atomic_load(&partial[(static_cast<size_t>(kk) * 2 + mm[k]) * f + col[k]],
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < a.splits) tot += pv[u];
+    }
+    sv[tid + k * kThreads] = tot;
+  }
   __syncthreads();
-  if (tid < kPanel) {
-    const float uu = sv[tid];
-    const float gg = sv[kPanel + tid];
+  for (int c = tid; c < kPw; c += kThreads) {  // wave-uniform trip count
+    const float uu = sv[c];
+    const float gg = sv[kPw + c];
     const float st = uu * silu_f32(gg);
-    if (kWriteState) a.s_tilde[static_cast<size_t>(b) * f + col] = st;
+    const size_t gc = static_cast<size_t>(panel) * kPw + c;
+    if (kWriteState) a.s_tilde[static_cast<size_t>(b) * f + gc] = st;
     const uint64_t bal = __ballot(fabsf(st) >= a.tau_s);
     if (lane == 0) {
-      bitmap[panel * (kPanel / 32) + wave * 2] = static_cast<uint32_t>(bal);
-      bitmap[panel * (kPanel / 32) + wave * 2 + 1] = static_cast<uint32_t>(bal >> 32);
+      const size_t w0 = (gc - lane) / 32;
+      bitmap[w0] = static_cast<uint32_t>(bal);
+      bitmap[w0 + 1] = static_cast<uint32_t>(bal >> 32);
     }
   }
   if (tid == 0) {
@@ -247,17 +272,23 @@ hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_
   const size_t kept_bytes = static_cast<size_t>(a.rows_per_split) * sizeof(KeptRow);
   const size_t red_bytes = static_cast<size_t>(32) * kRedStride * sizeof(float);
   const size_t smem = kept_bytes > red_bytes ? kept_bytes : red_bytes;
+#define PROX_S1_LAUNCH(TAG, WS, PW) \
+  hipLaunchKernelGGL((stage1_kernel<TAG, WS, PW>), grid, dim3(kThreads), smem, s, a)
+  const bool wide = a.panel == 256;
   if (wdtype == PROX_BF16) {
-    if (write_state)
-      hipLaunchKernelGGL((stage1_kernel<Bf16Tag, true>), grid, dim3(kThreads), smem, s, a);
-    else
-      hipLaunchKernelGGL((stage1_kernel<Bf16Tag, false>), grid, dim3(kThreads), smem, s, a);
+    if (write_state) {
+      if (wide) PROX_S1_LAUNCH(Bf16Tag, true, 256); else PROX_S1_LAUNCH(Bf16Tag, true, 128);
+    } else {
+      if (wide) PROX_S1_LAUNCH(Bf16Tag, false, 256); else PROX_S1_LAUNCH(Bf16Tag, false, 128);
+    }
   } else {
-    if (write_state)
-      hipLaunchKernelGGL((stage1_kernel<F32Tag, true>), grid, dim3(kThreads), smem, s, a);
-    else
-      hipLaunchKernelGGL((stage1_kernel<F32Tag, false>), grid, dim3(kThreads), smem, s, a);
+    if (write_state) {
+      if (wide) PROX_S1_LAUNCH(F32Tag, true, 256); else PROX_S1_LAUNCH(F32Tag, true, 128);
+    } else {
+      if (wide) PROX_S1_LAUNCH(F32Tag, false, 256); else PROX_S1_LAUNCH(F32Tag, false, 128);
+    }
   }
+#undef PROX_S1_LAUNCH
   return hipGetLastError();
 }
 

@@ -101,6 +101,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
       sv[u] = (i0 + u * kWaves < n && j >= 0 && cvalid) ? sr[i] : 0.f;
       w[u] = ldg16(Wd + static_cast<size_t>(j >= 0 ? j : 0) * d + colc);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
 #pragma unroll
     for (int u = 0; u < kDownUnroll; ++u) axpy16<T>(acc, sv[u], w[u]);
   }

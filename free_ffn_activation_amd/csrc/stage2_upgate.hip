@@ -26,6 +26,9 @@
 namespace prox {
 namespace {
 
+// bitmap words held per thread: d_ff <= 65536 gives 2048 words over 256 threads
+constexpr int kMaxWordsPerThread = 8;
+
 // Inclusive block scan of one int per thread; returns the inclusive prefix and
 // writes the block total to *total.  `scratch` holds 4 ints.
 __device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* total) {
@@ -63,8 +66,7 @@ __global__ __launch_bounds__(kThreads) void upgate_kernel(UpGateArgs a) {
   const int nw = f / 32;
 
   uint4* xs = reinterpret_cast<uint4*>(smem);
-  int* pre = reinterpret_cast<int*>(smem + static_cast<size_t>(nchunks) * 16);
-  int* jl = pre + (kFromBitmap ? nw + 1 : 0);
+  int* jl = reinterpret_cast<int*>(smem + static_cast<size_t>(nchunks) * 16);
 
   // x -> LDS
   const uint4* xg = reinterpret_cast<const uint4*>(static_cast<const S*>(a.x) +
@@ -74,24 +76,26 @@ __global__ __launch_bounds__(kThreads) void upgate_kernel(UpGateArgs a) {
   for (int c = blockIdx.x * kThreads + tid; c < d; c += gridDim.x * kThreads)
     a.y[static_cast<size_t>(b) * d + c] = 0.f;
 
-  // number of kept channels and (decode mode) the word prefix of the bitmap
+  // Decode mode: each thread keeps a run of consecutive bitmap words in
+  // registers; one block scan of their popcounts gives every word's ordinal
+  // offset, and the thread then emits the kept channels of its own words that
+  // fall in this block's ordinal range.  One global round trip in total.
   int ks = 0;
-  const uint32_t* bm = reinterpret_cast<const uint32_t*>(
-      a.ws + static_cast<size_t>(b) * a.tok_bytes + a.off_bitmap);
+  uint32_t wv[kMaxWordsPerThread];
+  int w0 = 0, run = 0;
   if (kFromBitmap) {
+    const uint32_t* bm = reinterpret_cast<const uint32_t*>(
+        a.ws + static_cast<size_t>(b) * a.tok_bytes + a.off_bitmap);
     const int per = (nw + kThreads - 1) / kThreads;
-    const int w0 = min(nw, tid * per);
-    const int w1 = min(nw, w0 + per);
+    w0 = min(nw, tid * per);
     int local = 0;
-    for (int w = w0; w < w1; ++w) local += __popc(bm[w]);
-    int total = 0;
-    const int incl = block_inclusive_scan(local, s_scan, &total);
-    int run = incl - local;
-    for (int w = w0; w < w1; ++w) {
-      pre[w] = run;
-      run += __popc(bm[w]);
+#pragma unroll
+    for (int k = 0; k < kMaxWordsPerThread; ++k) {
+      wv[k] = (k < per && w0 + k < nw) ? bm[w0 + k] : 0u;
+      local += __popc(wv[k]);
     }
-    if (tid == 0) pre[nw] = total;
+    int total = 0;
+    run = block_inclusive_scan(local, s_scan, &total) - local;
     ks = total;
   } else {
     ks = min(max(a.mask_count[b], 0), f);
@@ -100,18 +104,21 @@ __global__ __launch_bounds__(kThreads) void upgate_kernel(UpGateArgs a) {
   const int k0 = min(ks, static_cast<int>(blockIdx.x) * cpb);
   const int k1 = min(ks, k0 + cpb);
   const int nloc = k1 - k0;
-  __syncthreads();
 
   if (kFromBitmap) {
     if (blockIdx.x == 0 && tid == 0) a.mask_count[b] = ks;
-    for (int w = tid; w < nw; w += kThreads) {
-      int o = pre[w];
-      uint32_t bits = bm[w];
-      if (o >= k1 || o + __popc(bits) <= k0) continue;
+    int o = run;
+#pragma unroll
+    for (int k = 0; k < kMaxWordsPerThread; ++k) {
+      uint32_t bits = wv[k];
+      if (o >= k1 || o + __popc(bits) <= k0) {
+        o += __popc(bits);
+        continue;
+      }
       while (bits) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1u;
-        if (o >= k0 && o < k1) jl[o - k0] = w * 32 + bit;
+        if (o >= k0 && o < k1) jl[o - k0] = (w0 + k) * 32 + bit;
         ++o;
       }
     }
@@ -141,6 +148,9 @@ __global__ __launch_bounds__(kThreads) void upgate_kernel(UpGateArgs a) {
           lu[u] = ldg16(wu + cidx);
           lg[u] = ldg16(wg + cidx);
         }
+        // keep the whole batch in flight: the scheduler would otherwise sink
+        // each load next to its use and serialise the memory round trips
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kUpGateUnroll; ++u) {
           const int cidx = (s0 + u) * 64 + lane;
@@ -167,9 +177,7 @@ hipError_t launch_upgate(const UpGateArgs& a, int wdtype, int batch, int blocks,
                          bool from_bitmap, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(batch));
   const size_t esz = wdtype == PROX_BF16 ? 2 : 4;
-  const size_t smem = static_cast<size_t>(a.d) * esz +
-                      (from_bitmap ? static_cast<size_t>(a.f / 32 + 1) * 4 : 0) +
-                      static_cast<size_t>(a.max_cpb) * 4;
+  const size_t smem = static_cast<size_t>(a.d) * esz + static_cast<size_t>(a.max_cpb) * 4;
   if (wdtype == PROX_BF16) {
     if (from_bitmap)
       hipLaunchKernelGGL((upgate_kernel<Bf16Tag, true>), grid, dim3(kThreads), smem, s, a);
