@@ -50,6 +50,53 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = {
+    "stage1_proxy": "stage1.hip",
+    "stage2_upgate": "stage2_upgate.hip",
+    "stage2_down": "stage2_down.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 over the sources that define a kernel's code."""
+    import hashlib
+    csrc = os.path.join(ROOT, "free_ffn_activation_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kernel], "prox_device.h", "prox_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, algorithmic_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    measurement, or None when there is none for this kernel or the kernel's
+    sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return {"bytes_per_launch": rec["hbm_bytes_per_launch"],
+            "fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
+            "vs_algorithmic": round(rec["hbm_bytes_per_launch"] / algorithmic_bytes, 3)}
+
+
+def pmc_copy(n_bytes: int, reps: int) -> None:
+    """Device-to-device copies of a known size, the scale reference for the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n_bytes} bytes {reps} times")
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,6 +109,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-copy-mib", type=int, default=0,
+                    help="only run device copies of this many MiB (counter scale reference)")
     return ap.parse_args()
 
 
@@ -70,6 +119,9 @@ def main() -> int:
     if args.gpus != 1:
         sys.exit(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
                  "(the decode path has no multi-GPU mode)")
+    if args.pmc_copy_mib:
+        pmc_copy(args.pmc_copy_mib << 20, 4)
+        return 0
 
     import numpy as np
     import torch
@@ -198,34 +250,63 @@ def main() -> int:
     else:
         prox_us, timed_steps, wall = time_graph(step, "prox graph")
 
-    # ---------------------------------------------------------------- per-kernel events
-    n_ev = min(steps_per_round, 256)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
-    for row in evs:  # torch creates the underlying HIP event on first record
-        for ev in row:
-            ev.record()
+    # ---------------------------------------------------------------- per-kernel timing
+    # Each kernel alone, launched back to back from a graph over the same
+    # rotation: every schedule step owns a workspace and outputs prepared by
+    # one full decode, so a single stage can be replayed on it
+    # (prox_ffn_decode_stages).  HIP events bracket the replays on the stream
+    # the kernels run on.
+    n_iso = steps_per_round
+    iso_ws = [prox.new_workspace(d, f, 1) for _ in range(n_iso)]
+    iso_out = [(torch.empty(1, d, dtype=torch.float32, device=dev),
+                torch.empty(1, f, dtype=torch.int32, device=dev),
+                torch.empty(1, dtype=torch.int32, device=dev),
+                torch.empty(1, dtype=torch.int32, device=dev)) for _ in range(n_iso)]
+
+    def staged(stages):
+        def fn(s):
+            l, t = sched[s % steps_per_round]
+            tx, ts = taus[l]
+            yy, mm, cc, ii = iso_out[s % n_iso]
+            prox.prox_ffn_decode_stages(layers[l], xs[l][t], tx, ts, yy, mm, cc, ii,
+                                        iso_ws[s % n_iso], stages)
+        return fn
+
+    full = staged(7)
+    for s in range(n_iso):
+        full(s)
     torch.cuda.synchronize()
-    torch.cuda._sleep(100_000_000)  # keep the GPU busy while the host enqueues
-    for s in range(n_ev):
-        l, t = sched[s]
-        tx, ts = taus[l]
-        prox.prox_ffn_decode_events(layers[l], xs[l][t], tx, ts, y, mi, mc, ic, ws, evs[s])
-    torch.cuda.synchronize()
-    k_us = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for i in range(3)]
-                     for s in range(n_ev)])
-    k_mean = k_us.mean(axis=0)
-    step_ev_us = np.array([evs[s][0].elapsed_time(evs[s][3]) * 1e3 for s in range(n_ev)])
-    log("kernel split (us, mean): stage1 %.2f  upgate %.2f  down %.2f  (event-bracketed step %.2f)"
-        % (k_mean[0], k_mean[1], k_mean[2], step_ev_us.mean()))
-    sub = sched[:n_ev]
-    bytes_k = [float(np.mean([a[l, t] for (l, t) in sub])) for a in (by_stage1, by_upgate, by_down)]
     names = ["stage1_proxy", "stage2_upgate", "stage2_down"]
+    stage_bits = [prox.PROX_STAGE_PROXY, prox.PROX_STAGE_UPGATE, prox.PROX_STAGE_DOWN]
+    k_mean = []
+    for nm, bit in zip(names, stage_bits):
+        if args.no_graph:
+            fn = staged(bit)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s in range(K):
+                fn(s)
+            torch.cuda.synchronize()
+            k_mean.append((time.perf_counter() - t0) / K * 1e6)
+        else:
+            k_mean.append(time_graph(staged(bit), f"{nm} alone")[0])
+    # the up/gate kernel zeroes y, so replaying the down kernel alone keeps adding
+    # into it; restore every output with one full pass
+    for s in range(n_iso):
+        full(s)
+    torch.cuda.synchronize()
+    k_mean = np.array(k_mean)
+    log("kernel split (us, each alone): stage1 %.2f  upgate %.2f  down %.2f  (sum %.2f)"
+        % (k_mean[0], k_mean[1], k_mean[2], k_mean.sum()))
+    bytes_k = [sched_mean(a) for a in (by_stage1, by_upgate, by_down)]
     dom = int(np.argmax(k_mean))
     ach = bytes_k[dom] / (k_mean[dom] * 1e-6) / 1e9
     kernels = {names[i]: {"us": round(float(k_mean[i]), 3),
                           "algorithmic_MB": round(bytes_k[i] / 1e6, 3),
                           "GBps": round(bytes_k[i] / (k_mean[i] * 1e-6) / 1e9, 1)}
                for i in range(3)}
+    del iso_ws, iso_out
+    traffic = measured_traffic(names[dom], bytes_k[dom])
 
     # ---------------------------------------------------------------- dense comparators
     dense = {}
@@ -308,7 +389,7 @@ def main() -> int:
         "dense_us_per_layer": dense,
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

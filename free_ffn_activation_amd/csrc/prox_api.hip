@@ -150,7 +150,7 @@ DownArgs down_args(const Plan& p, const prox_layer* L, void* ws, const int* mask
 prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, float tau_x,
                         float tau_s, float* y, int32_t* mask_idx, int32_t* mask_count,
                         int32_t* in_count, void* ws, size_t ws_bytes, void* stream,
-                        void* const* events) {
+                        void* const* events, int32_t stages = 7) {
   prox_status st = check_layer(layer);
   if (st != PROX_OK) return st;
   if ((st = check_batch(batch)) != PROX_OK) return st;
@@ -167,22 +167,30 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
     for (int i = 0; i < 4; ++i)
       if (!events[i]) return fail(PROX_ERR_INVALID_ARG, "events[%d] is NULL", i);
   }
+  if (stages < 1 || stages > 7)
+    return fail(PROX_ERR_INVALID_ARG, "stages %d is not a non-empty subset of 1|2|4", stages);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  e = launch_stage1(stage1_args(p, layer, x, tau_x, tau_s, ws, nullptr, in_count), layer->wdtype,
-                    batch, false, s);
-  if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
+  if (stages & PROX_STAGE_PROXY) {
+    e = launch_stage1(stage1_args(p, layer, x, tau_x, tau_s, ws, nullptr, in_count), layer->wdtype,
+                      batch, false, s);
+    if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
+  }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  e = launch_upgate(upgate_args(p, layer, x, ws, mask_idx, mask_count, y), layer->wdtype, batch,
-                    p.ug_blocks, true, s);
-  if (e != hipSuccess) return hip_fail(e, "stage-2 up/gate launch");
+  if (stages & PROX_STAGE_UPGATE) {
+    e = launch_upgate(upgate_args(p, layer, x, ws, mask_idx, mask_count, y), layer->wdtype, batch,
+                      p.ug_blocks, true, s);
+    if (e != hipSuccess) return hip_fail(e, "stage-2 up/gate launch");
+  }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[2]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, s);
-  if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
+  if (stages & PROX_STAGE_DOWN) {
+    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, s);
+    if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
+  }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[3]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   return PROX_OK;
@@ -468,6 +476,19 @@ PROX_API prox_status prox_ffn_decode_events(const prox_layer* layer, const void*
     if (!events) return fail(PROX_ERR_INVALID_ARG, "events is NULL");
     return decode_impl(layer, x, batch, tau_x, tau_s, y, mask_idx, mask_count, in_count, ws, ws_bytes,
                        stream, events);
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_ffn_decode_stages(const prox_layer* layer, const void* x, int32_t batch,
+                                            float tau_x, float tau_s, float* y, int32_t* mask_idx,
+                                            int32_t* mask_count, int32_t* in_count, void* ws,
+                                            size_t ws_bytes, void* stream, int32_t stages) {
+  try {
+    g_err.clear();
+    return decode_impl(layer, x, batch, tau_x, tau_s, y, mask_idx, mask_count, in_count, ws, ws_bytes,
+                       stream, nullptr, stages);
   } catch (...) {
     return fail(PROX_ERR_INTERNAL, "unexpected exception");
   }

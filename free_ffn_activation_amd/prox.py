@@ -23,14 +23,17 @@ PROX_ERR_HIP = -3
 PROX_ERR_INTERNAL = -4
 PROX_F32 = 0
 PROX_BF16 = 1
+PROX_STAGE_PROXY = 1
+PROX_STAGE_UPGATE = 2
+PROX_STAGE_DOWN = 4
 
 _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPORTED",
                  -3: "PROX_ERR_HIP", -4: "PROX_ERR_INTERNAL"}
 
 EXPORTED = ("prox_abi_version", "prox_last_error", "prox_layer_sizes", "prox_workspace_size",
             "prox_calibrate_workspace_size", "prox_workspace_init", "prox_pack_proxy",
-            "prox_calibrate", "prox_ffn_decode", "prox_ffn_decode_events", "prox_ffn_stage2",
-            "prox_proxy_state")
+            "prox_calibrate", "prox_ffn_decode", "prox_ffn_decode_events",
+            "prox_ffn_decode_stages", "prox_ffn_stage2", "prox_proxy_state")
 
 
 class ProxError(RuntimeError):
@@ -68,6 +71,8 @@ _sig = {
                                  _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "prox_ffn_decode_events": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_vp,
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp, _P(_c_vp)]),
+    "prox_ffn_decode_stages": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_vp,
+                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp, _c_i32]),
     "prox_ffn_stage2": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
                                  _c_size, _c_vp]),
     "prox_proxy_state": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp,
@@ -233,6 +238,17 @@ def prox_ffn_decode_events(layer: ProxLayer, x: torch.Tensor, tau_x: float, tau_
                                        _ptr(y), _ptr(mask_idx), _ptr(mask_count), _ptr(in_count),
                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
                                        handles))
+
+
+def prox_ffn_decode_stages(layer: ProxLayer, x: torch.Tensor, tau_x: float, tau_s: float,
+                           y: torch.Tensor, mask_idx: torch.Tensor, mask_count: torch.Tensor,
+                           in_count: torch.Tensor | None, ws: torch.Tensor, stages: int,
+                           stream=None) -> None:
+    """Run the decode kernels selected by `stages` (PROX_STAGE_* bits)."""
+    b = _decode_args(layer, x, y, mask_idx, mask_count, in_count)
+    _check(_lib.prox_ffn_decode_stages(ctypes.byref(layer.desc), _ptr(x), b, tau_x, tau_s, _ptr(y),
+                                       _ptr(mask_idx), _ptr(mask_count), _ptr(in_count), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream), stages))
 
 
 def prox_ffn_stage2(layer: ProxLayer, x: torch.Tensor, mask_idx: torch.Tensor,

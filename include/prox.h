@@ -178,6 +178,25 @@ prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32
                                    size_t ws_bytes, void* stream, void* const* events);
 
 /*
+ * Runs a subset of the three decode kernels, for profiling one kernel alone.
+ *   stages      bit mask: PROX_STAGE_PROXY (Stage 1: input mask, INT4 proxy,
+ *               channel bitmap in ws, in_count), PROX_STAGE_UPGATE (channel
+ *               list from the bitmap -> mask_idx, mask_count; s_j in ws; zeroes
+ *               y), PROX_STAGE_DOWN (accumulates y from mask_idx, mask_count and
+ *               the s_j in ws).  7 is prox_ffn_decode.
+ * A stage run without its predecessors reads what an earlier call with the
+ * same layer, x, thresholds, outputs and workspace left there.  Other
+ * arguments as prox_ffn_decode.  Asynchronous.
+ */
+#define PROX_STAGE_PROXY 1
+#define PROX_STAGE_UPGATE 2
+#define PROX_STAGE_DOWN 4
+prox_status prox_ffn_decode_stages(const prox_layer* layer, const void* x, int32_t batch,
+                                   float tau_x, float tau_s, float* y, int32_t* mask_idx,
+                                   int32_t* mask_count, int32_t* in_count, void* ws,
+                                   size_t ws_bytes, void* stream, int32_t stages);
+
+/*
  * Stage 2 alone ([blog] "Stage 2") from a caller-given channel list.
  *   mask_idx    device [batch][d_ff] int32, ascending indices in [0, d_ff);
  *               entries outside that range are skipped

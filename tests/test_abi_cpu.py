@@ -120,3 +120,7 @@ def test_other_entry_points_validate():
     assert lib.prox_ffn_decode_events(ctypes.byref(L), FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE, None,
                                       FAKE, 1 << 30, None, None) == P.PROX_ERR_INVALID_ARG
     assert lib.prox_workspace_init(None, 16, None) == P.PROX_ERR_INVALID_ARG
+    # stage subsets must be a non-empty subset of the three kernels
+    for bad in (0, 8, -1):
+        assert lib.prox_ffn_decode_stages(ctypes.byref(L), FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE,
+                                          None, FAKE, 1 << 30, None, bad) == P.PROX_ERR_INVALID_ARG

@@ -344,3 +344,29 @@ def test_graph_replay_matches_eager(P, name):
         torch.cuda.synchronize()
         assert int(mc2.item()) == eager[rep % len(xs)][2]
     del g
+
+
+def test_decode_stages_compose(P):
+    """Stages run one at a time on the same workspace give prox_ffn_decode."""
+    layer, ov = oracle_layer("qwen3_8b")
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov, n_tok=16)
+    x = to_device(layer.x_dec[[5]], "bf16")
+    ws = P.new_workspace(L.d_model, L.d_ff, 1)
+    y, mi, mc, ic = _bufs(P, L, 1)
+    P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, ws)
+    torch.cuda.synchronize()
+    ref = (y.cpu().numpy(), mi.cpu().numpy(), int(mc.item()), int(ic.item()))
+    ws2 = P.new_workspace(L.d_model, L.d_ff, 1)
+    y2, mi2, mc2, ic2 = _bufs(P, L, 1)
+    for bit in (P.PROX_STAGE_PROXY, P.PROX_STAGE_UPGATE, P.PROX_STAGE_DOWN):
+        P.prox_ffn_decode_stages(L, x, tau_x, tau_s, y2, mi2, mc2, ic2, ws2, bit)
+        torch.cuda.synchronize()
+    assert int(mc2.item()) == ref[2] and int(ic2.item()) == ref[3]
+    assert np.array_equal(mi2.cpu().numpy()[0, :ref[2]], ref[1][0, :ref[2]])
+    ma, rl = y_errors(y2.cpu().numpy()[0], ref[0][0].astype(np.float64))
+    assert rl <= 1e-6
+    # replaying the up/gate stage alone re-derives the same list from the bitmap
+    P.prox_ffn_decode_stages(L, x, tau_x, tau_s, y2, mi2, mc2, ic2, ws2, P.PROX_STAGE_UPGATE)
+    torch.cuda.synchronize()
+    assert int(mc2.item()) == ref[2] and np.array_equal(mi2.cpu().numpy()[0, :ref[2]], ref[1][0, :ref[2]])
