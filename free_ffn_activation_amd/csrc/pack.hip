@@ -5,6 +5,9 @@
 // and gate proxies are symmetric per-row INT4 copies kept resident on the GPU;
 // W_down has none).  A row is a row of the [d_model, d_ff] matrix, i.e. one
 // input coordinate, so Stage 1 reads one contiguous run per kept coordinate.
+// Rows are qstride bytes apart (an odd multiple of 128): Stage 1 reads one
+// 128-byte column slice from many rows, and a stride with a large power-of-two
+// factor would send all of a slice's reads to a few HBM channels.
 // scale = fp32(absmax / 7); code = clamp(rint_half_even(fp32(w / scale)),
 // -7, 7) with IEEE-rounded fp32 divisions; a zero row has scale 0, codes 0.
 #include "prox_device.h"
@@ -23,7 +26,8 @@ __device__ __forceinline__ int quant_code(float w, float sc) {
 // then the packed 16-byte groups (8 bytes up codes, 8 bytes gate codes).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const void* wu, const void* wg, int d,
-                                                              int f, uint8_t* q, float* scale) {
+                                                              int f, int qstride, uint8_t* q,
+                                                              float* scale) {
   __shared__ float s_max[2][4];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -61,9 +65,12 @@ __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const void* wu, con
       up[k >> 3] |= nu << (4 * (k & 7));
       gt[k >> 3] |= ng << (4 * (k & 7));
     }
-    *reinterpret_cast<uint4*>(q + rb + static_cast<size_t>(g) * 16) =
+    *reinterpret_cast<uint4*>(q + static_cast<size_t>(i) * qstride + static_cast<size_t>(g) * 16) =
         make_uint4(up[0], up[1], gt[0], gt[1]);
   }
+  // zero the row's padding bytes (qstride - f, a multiple of 16)
+  for (int o = f + tid * 16; o < qstride; o += kThreads * 16)
+    *reinterpret_cast<uint4*>(q + static_cast<size_t>(i) * qstride + o) = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // dst[j][which][i] = src[i][j] for src [d][f]; 64x64 tiles through LDS.
@@ -110,19 +117,19 @@ __global__ __launch_bounds__(kThreads) void digit_hist_kernel(const void* v, siz
 
 }  // namespace
 
-hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int wdtype,
+hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int qstride, int wdtype,
                        uint8_t* proxy_q, float* proxy_scale, void* w_upgate_t, hipStream_t s) {
   const dim3 tgrid(static_cast<unsigned>(f / 64), static_cast<unsigned>(d / 64));
   if (wdtype == PROX_BF16) {
     hipLaunchKernelGGL((pack_rows_kernel<Bf16Tag>), dim3(d), dim3(kThreads), 0, s, w_up, w_gate, d, f,
-                       proxy_q, proxy_scale);
+                       qstride, proxy_q, proxy_scale);
     hipLaunchKernelGGL((transpose_kernel<uint16_t>), tgrid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(w_up), d, f, static_cast<uint16_t*>(w_upgate_t), 0);
     hipLaunchKernelGGL((transpose_kernel<uint16_t>), tgrid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(w_gate), d, f, static_cast<uint16_t*>(w_upgate_t), 1);
   } else {
     hipLaunchKernelGGL((pack_rows_kernel<F32Tag>), dim3(d), dim3(kThreads), 0, s, w_up, w_gate, d, f,
-                       proxy_q, proxy_scale);
+                       qstride, proxy_q, proxy_scale);
     hipLaunchKernelGGL((transpose_kernel<float>), tgrid, dim3(kThreads), 0, s,
                        static_cast<const float*>(w_up), d, f, static_cast<float*>(w_upgate_t), 0);
     hipLaunchKernelGGL((transpose_kernel<float>), tgrid, dim3(kThreads), 0, s,

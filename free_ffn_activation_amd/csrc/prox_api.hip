@@ -94,6 +94,7 @@ Stage1Args stage1_args(const Plan& p, const prox_layer* L, const void* x, float 
   a.rows_per_split = p.rows_per_split;
   a.n_panels = p.n_panels;
   a.panel = p.panel;
+  a.proxy_stride = p.proxy_stride;
   a.proxy_q = static_cast<const uint8_t*>(L->proxy_q);
   a.proxy_scale = L->proxy_scale;
   a.x = x;
@@ -137,10 +138,12 @@ DownArgs down_args(const Plan& p, const prox_layer* L, void* ws, const int* mask
   a.col_slices = p.dn_col_slices;
   a.row_groups = p.dn_row_groups;
   a.max_rows = p.dn_max_rows;
+  a.chan_per_group = p.dn_chan_per_group;
   a.w_down = L->w_down;
   a.ws = static_cast<const uint8_t*>(ws);
   a.tok_bytes = p.tok_bytes;
   a.off_ssp = p.off_ssp;
+  a.off_bitmap = p.off_bitmap;
   a.mask_idx = mask_idx;
   a.mask_count = mask_count;
   a.y = y;
@@ -188,7 +191,7 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[2]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   if (stages & PROX_STAGE_DOWN) {
-    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, s);
+    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, true, s);
     if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
   }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[3]), s)) != hipSuccess)
@@ -256,11 +259,14 @@ size_t calib_bytes(const Plan& p, int32_t n_tokens) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
+int proxy_row_stride(int f) { return ((f / 128) % 2 == 1) ? f : f + 128; }
+
 Plan make_plan(int d, int f, int wdtype) {
   Plan p;
   p.d = d;
   p.f = f;
   p.wdtype = wdtype;
+  p.proxy_stride = proxy_row_stride(f);
   // 128-column panels: wider panels gather faster but double the split
   // partials and the last block's reduction, which costs more than it saves
   p.panel = 128;
@@ -271,7 +277,7 @@ Plan make_plan(int d, int f, int wdtype) {
   splits = std::max(1, std::min(64, splits));
   int rps = (d + splits - 1) / splits;
   rps = (rps + 63) / 64 * 64;
-  rps = std::min(rps, 4096);  // bounds the LDS list of kept rows
+  rps = std::min(rps, 2048);  // bounds the LDS list of kept rows (20 B per row)
   p.rows_per_split = rps;
   p.splits = (d + rps - 1) / rps;
   // up/gate: enough 4-wave blocks for one kept channel per wave at ~30% keep
@@ -287,8 +293,12 @@ Plan make_plan(int d, int f, int wdtype) {
   const int red_bytes = (kDownThreads / 64) * cw * 4;
   const int max_rows_cap = (61440 - red_bytes) / 8;
   rg = std::max(rg, (f + max_rows_cap - 1) / max_rows_cap);
+  // decode mode: a row group is a channel range of at most one channel per thread
+  rg = std::max(rg, (f + kDownThreads - 1) / kDownThreads);
+  p.dn_chan_per_group = ((f + rg - 1) / rg + 31) / 32 * 32;
+  rg = (f + p.dn_chan_per_group - 1) / p.dn_chan_per_group;
   p.dn_row_groups = rg;
-  p.dn_max_rows = (f + rg - 1) / rg;
+  p.dn_max_rows = std::max((f + rg - 1) / rg, p.dn_chan_per_group);
   // per-token workspace slice
   size_t off = 0;
   p.off_tickets = off;
@@ -320,7 +330,7 @@ PROX_API prox_status prox_layer_sizes(int32_t d, int32_t f, int32_t wdtype, size
     prox_status st = check_shape(d, f, wdtype);
     if (st != PROX_OK) return st;
     const size_t es = elem_size(wdtype);
-    bytes_out[0] = static_cast<size_t>(d) * f;
+    bytes_out[0] = static_cast<size_t>(d) * proxy_row_stride(f);
     bytes_out[1] = static_cast<size_t>(2) * d * sizeof(float);
     bytes_out[2] = static_cast<size_t>(2) * f * d * es;
     bytes_out[3] = static_cast<size_t>(f) * d * es;
@@ -385,7 +395,8 @@ PROX_API prox_status prox_pack_proxy(const void* W_up, const void* W_gate, const
       return fail(PROX_ERR_INVALID_ARG, "input weights must be 16-byte aligned");
     const int d = out->d_model, f = out->d_ff;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_pack(W_up, W_gate, d, f, out->wdtype, static_cast<uint8_t*>(out->proxy_q),
+    hipError_t e = launch_pack(W_up, W_gate, d, f, proxy_row_stride(f), out->wdtype,
+                               static_cast<uint8_t*>(out->proxy_q),
                                out->proxy_scale, out->w_upgate_t, s);
     if (e != hipSuccess) return hip_fail(e, "pack launch");
     if (out->w_down != W_down) {
@@ -514,7 +525,7 @@ PROX_API prox_status prox_ffn_stage2(const prox_layer* layer, const void* x, int
     hipError_t e = launch_upgate(upgate_args(p, layer, x, ws, mi, mc, y), layer->wdtype, batch,
                                  p.ug_blocks, false, s);
     if (e != hipSuccess) return hip_fail(e, "stage-2 up/gate launch");
-    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, s);
+    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, false, s);
     if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
     return PROX_OK;
   } catch (...) {

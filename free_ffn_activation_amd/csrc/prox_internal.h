@@ -24,6 +24,7 @@ constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column
 struct Plan {
   int d, f, wdtype;
   // Stage 1
+  int proxy_stride;  // bytes between proxy rows (odd multiple of 128)
   int panel;         // Stage-1 output columns per block (256 or 128)
   int n_panels;      // f / panel
   int splits;        // K-splits over input rows
@@ -34,7 +35,8 @@ struct Plan {
   // Stage 2 down
   int dn_col_slices; // ceil(d / column-slice width)
   int dn_row_groups;
-  int dn_max_rows;   // max rows per group
+  int dn_max_rows;   // max rows per group (list mode) / LDS rows
+  int dn_chan_per_group;  // decode mode: channels per row group (multiple of 32, <= 1024)
   // workspace layout, bytes per token and offsets inside a token's slice
   size_t tok_bytes;
   size_t off_tickets, off_kcount, off_partial, off_bitmap, off_ssp;
@@ -43,7 +45,7 @@ struct Plan {
 Plan make_plan(int d, int f, int wdtype);
 
 struct Stage1Args {
-  int d, f, splits, rows_per_split, n_panels, panel;
+  int d, f, splits, rows_per_split, n_panels, panel, proxy_stride;
   const uint8_t* proxy_q;
   const float* proxy_scale;
   const void* x;          // [batch][d]
@@ -67,10 +69,10 @@ struct UpGateArgs {
 };
 
 struct DownArgs {
-  int d, f, col_slices, row_groups, max_rows;
+  int d, f, col_slices, row_groups, max_rows, chan_per_group;
   const void* w_down;     // [f][d]
-  const uint8_t* ws;      // s_sp
-  size_t tok_bytes, off_ssp;
+  const uint8_t* ws;      // s (by channel in decode mode, by list position otherwise), bitmap
+  size_t tok_bytes, off_ssp, off_bitmap;
   const int* mask_idx;
   const int* mask_count;
   float* y;
@@ -81,8 +83,9 @@ hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_
                          hipStream_t s);
 hipError_t launch_upgate(const UpGateArgs& a, int wdtype, int batch, int blocks,
                          bool from_bitmap, hipStream_t s);
-hipError_t launch_down(const DownArgs& a, int wdtype, int batch, hipStream_t s);
-hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int wdtype,
+hipError_t launch_down(const DownArgs& a, int wdtype, int batch, bool from_bitmap, hipStream_t s);
+int proxy_row_stride(int f);
+hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int qstride, int wdtype,
                        uint8_t* proxy_q, float* proxy_scale, void* w_upgate_t, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // Calibration helpers: histogram of 8-bit digits of |v| keys that match a

@@ -47,10 +47,10 @@
 namespace prox {
 namespace {
 
-struct KeptRow {
-  int row;
-  float a_up;
-  float a_gate;
+// A kept input row as the gather loop consumes it: a = x_i * scale_i of both
+// proxies pre-multiplied by 2^24 and 2^20, and the row's byte offset.
+struct KeptA {
+  float u24, u20, g24, g20;
 };
 
 constexpr int kRedStride = kThreads + 1;  // LDS row of the cross-slot reduction
@@ -88,8 +88,11 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int b = blockIdx.y;
-  const int panel = blockIdx.x / a.splits;
-  const int split = blockIdx.x - panel * a.splits;
+  // split-major order: blocks dispatched together cover every panel of the
+  // same rows (DRAM page locality), and with a panel count divisible by 8 all
+  // splits of a panel share an XCD
+  const int split = blockIdx.x / a.n_panels;
+  const int panel = blockIdx.x - split * a.n_panels;
   const int d = a.d;
   const int f = a.f;
   uint8_t* tws = a.ws + static_cast<size_t>(b) * a.tok_bytes;
@@ -104,9 +107,13 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   const int row0 = split * a.rows_per_split;
   const int row1 = min(d, row0 + a.rows_per_split);
   const int wchunk = (a.rows_per_split + 3) / 4;
+  const int wcap = wchunk + 1;  // one zero-weight sentinel entry per wave
   const int wr0 = min(row1, row0 + wave * wchunk);
   const int wr1 = min(row1, wr0 + wchunk);
-  KeptRow* kept = reinterpret_cast<KeptRow*>(smem) + wave * wchunk;
+  KeptA* ka = reinterpret_cast<KeptA*>(smem) + wave * wcap;
+  uint32_t* koff = reinterpret_cast<uint32_t*>(reinterpret_cast<KeptA*>(smem) + 4 * wcap) + wave * wcap;
+  constexpr float k2p24 = 16777216.0f;
+  constexpr float k2p20 = 1048576.0f;
   int nkept = 0;
   float sum_up = 0.f, sum_gate = 0.f;
   for (int base = wr0; base < wr1; base += 64) {
@@ -120,10 +127,18 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     const float au = keep ? xv * sc_up : 0.f;
     const float ag = keep ? xv * sc_gate : 0.f;
     const uint64_t bal = __ballot(keep);
-    if (keep) kept[nkept + __popcll(bal & ((1ull << lane) - 1ull))] = KeptRow{i, au, ag};
+    if (keep) {
+      const int pos = nkept + __popcll(bal & ((1ull << lane) - 1ull));
+      ka[pos] = KeptA{au * k2p24, au * k2p20, ag * k2p24, ag * k2p20};
+      koff[pos] = static_cast<uint32_t>(i) * static_cast<uint32_t>(a.proxy_stride);
+    }
     nkept += __popcll(bal);
     sum_up += au;
     sum_gate += ag;
+  }
+  if (lane == 0) {  // slots past the end read row 0 with weight 0
+    ka[nkept] = KeptA{0.f, 0.f, 0.f, 0.f};
+    koff[nkept] = 0u;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -146,31 +161,25 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     acc_u[e] = 0.f;
     acc_g[e] = 0.f;
   }
-  constexpr float k2p24 = 16777216.0f;
-  constexpr float k2p20 = 1048576.0f;
   constexpr int kWaveSlots = 64 / kLpr;
-  // Loads are unconditional (a slot past the end re-reads the last kept row
-  // with weight 0) so the compiler can wait on them one at a time.
+  // Loads are unconditional (slots past the end read the sentinel) so the
+  // compiler can wait on them one at a time.
   for (int r0 = wslot; r0 < nkept; r0 += kWaveSlots * kStage1Unroll) {
     uint4 w[kStage1Unroll];
-    float au[kStage1Unroll], ag[kStage1Unroll];
+    KeptA av[kStage1Unroll];
 #pragma unroll
     for (int u = 0; u < kStage1Unroll; ++u) {
-      const int r = r0 + u * kWaveSlots;
-      const KeptRow kr = kept[min(r, nkept - 1)];
-      w[u] = ldg16(pbase + static_cast<size_t>(kr.row) * f);
-      au[u] = r < nkept ? kr.a_up : 0.f;
-      ag[u] = r < nkept ? kr.a_gate : 0.f;
+      const int rr = min(r0 + u * kWaveSlots, nkept);
+      av[u] = ka[rr];
+      w[u] = ldg16(pbase + koff[rr]);
     }
     __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
 #pragma unroll
     for (int u = 0; u < kStage1Unroll; ++u) {
-      const float u24 = au[u] * k2p24, u20 = au[u] * k2p20;
-      const float g24 = ag[u] * k2p24, g20 = ag[u] * k2p20;
-      acc_dword(acc_u + 0, w[u].x, u24, u20);
-      acc_dword(acc_u + 8, w[u].y, u24, u20);
-      acc_dword(acc_g + 0, w[u].z, g24, g20);
-      acc_dword(acc_g + 8, w[u].w, g24, g20);
+      acc_dword(acc_u + 0, w[u].x, av[u].u24, av[u].u20);
+      acc_dword(acc_u + 8, w[u].y, av[u].u24, av[u].u20);
+      acc_dword(acc_g + 0, w[u].z, av[u].g24, av[u].g20);
+      acc_dword(acc_g + 8, w[u].w, av[u].g24, av[u].g20);
     }
   }
 
@@ -269,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
 hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_state,
                          hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.n_panels * a.splits), static_cast<unsigned>(batch));
-  const size_t kept_bytes = static_cast<size_t>(a.rows_per_split) * sizeof(KeptRow);
+  const size_t kept_bytes =
+      static_cast<size_t>(a.rows_per_split + 4) * (sizeof(KeptA) + sizeof(uint32_t));
   const size_t red_bytes = static_cast<size_t>(32) * kRedStride * sizeof(float);
   const size_t smem = kept_bytes > red_bytes ? kept_bytes : red_bytes;
 #define PROX_S1_LAUNCH(TAG, WS, PW) \

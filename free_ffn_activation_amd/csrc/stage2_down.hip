@@ -8,10 +8,13 @@
 // gfx950 design:
 //   * W_down is row-major [f][d]: a kept channel is one contiguous d-long run.
 //   * grid = (column slices x row groups, batch).  A column slice is what one
-//     wave covers with one 16-B load per lane (512 bf16 / 256 fp32 columns);
-//     a row group is a contiguous range of the ascending kept list.  The block
-//     stages its (index, s_j) pairs in LDS; each of its 16 waves streams every
-//     16th row with 8 loads in flight and accumulates its columns in registers.
+//     wave covers with one 16-B load per lane (512 bf16 / 256 fp32 columns).
+//     In decode mode a row group is a fixed range of channels whose kept ones
+//     the block finds in the Stage-1 bitmap (s_j is stored by channel index),
+//     so no count or list has to be fetched first; with a caller-given list a
+//     row group is a contiguous range of that list.  The block stages its
+//     (index, s_j) pairs in LDS; each of its 16 waves streams every 16th row
+//     with 8 loads in flight and accumulates its columns in registers.
 //   * the 16 waves' partial rows are summed through LDS and the block adds its
 //     slice into y with fp32 atomics (y was zeroed by the up/gate kernel).
 //     Large blocks keep the atomic count (row groups x d) low: fp32 global
@@ -45,12 +48,14 @@ __device__ __forceinline__ void axpy16<F32Tag>(float* acc, float s, uint4 w) {
   acc[3] = fmaf(s, __uint_as_float(w.w), acc[3]);
 }
 
-template <typename T>
+template <typename T, bool kFromBitmap>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
   typedef typename T::storage S;
   constexpr int kEpl = 16 / sizeof(S);
   constexpr int kCw = 64 * kEpl;  // columns per slice
+  constexpr int kWaves = kDownThreads / 64;
   extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_cnt[kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -60,25 +65,50 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
   const int f = a.f;
   const int cs = blockIdx.x % a.col_slices;
   const int rg = blockIdx.x / a.col_slices;
-  const int ks = min(max(a.mask_count[b], 0), f);
-  const int per = (ks + a.row_groups - 1) / a.row_groups;
-  const int r0 = min(ks, rg * per);
-  const int r1 = min(ks, r0 + per);
-  const int n = r1 - r0;
-  if (n <= 0) return;  // block-uniform
-
-  constexpr int kWaves = kDownThreads / 64;
   float* red = reinterpret_cast<float*>(smem);                 // [kWaves][kCw]
   int* jr = reinterpret_cast<int*>(red + kWaves * kCw);        // [max_rows]
   float* sr = reinterpret_cast<float*>(jr + a.max_rows);       // [max_rows]
-  const float* ssp = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(b) * a.tok_bytes +
-                                                    a.off_ssp);
-  for (int i = tid; i < n; i += kDownThreads) {
-    const int j = a.mask_idx[static_cast<size_t>(b) * f + r0 + i];
-    const bool ok = j >= 0 && j < f;
-    jr[i] = ok ? j : -1;
-    sr[i] = ok ? ssp[r0 + i] : 0.f;
+  const uint8_t* tws = a.ws + static_cast<size_t>(b) * a.tok_bytes;
+  const float* ssp = reinterpret_cast<const float*>(tws + a.off_ssp);
+  int n = 0;
+  if (kFromBitmap) {
+    // decode mode: this block's rows are the kept channels of a fixed channel
+    // range; the bitmap word and s_j of each channel come in one round trip
+    // and a block ballot compacts them in ascending order
+    const int c0 = rg * a.chan_per_group;
+    const int c1 = min(f, c0 + a.chan_per_group);
+    const int j = c0 + tid;
+    const int jc = min(j, c1 - 1);
+    const uint32_t word = reinterpret_cast<const uint32_t*>(tws + a.off_bitmap)[jc >> 5];
+    const float sj = ssp[jc];
+    const bool kept = j < c1 && ((word >> (jc & 31)) & 1u);
+    const uint64_t bal = __ballot(kept);
+    if (lane == 0) s_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = 0;
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      if (w2 < wave) off += s_cnt[w2];
+      n += s_cnt[w2];
+    }
+    if (kept) {
+      const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
+      jr[pos] = j;
+      sr[pos] = sj;
+    }
+  } else {
+    const int ks = min(max(a.mask_count[b], 0), f);
+    const int per = (ks + a.row_groups - 1) / a.row_groups;
+    const int r0 = min(ks, rg * per);
+    const int r1 = min(ks, r0 + per);
+    n = r1 - r0;
+    for (int i = tid; i < n; i += kDownThreads) {
+      const int j = a.mask_idx[static_cast<size_t>(b) * f + r0 + i];
+      const bool ok = j >= 0 && j < f;
+      jr[i] = ok ? j : -1;
+      sr[i] = ok ? ssp[r0 + i] : 0.f;
+    }
   }
+  if (n <= 0) return;  // block-uniform
   __syncthreads();
 
   const int col = cs * kCw + lane * kEpl;
@@ -121,14 +151,21 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
 
 }  // namespace
 
-hipError_t launch_down(const DownArgs& a, int wdtype, int batch, hipStream_t s) {
+hipError_t launch_down(const DownArgs& a, int wdtype, int batch, bool from_bitmap, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.col_slices * a.row_groups), static_cast<unsigned>(batch));
   const int cw = wdtype == PROX_BF16 ? 512 : 256;
   const size_t smem = static_cast<size_t>(kDownThreads / 64) * cw * 4 + static_cast<size_t>(a.max_rows) * 8;
-  if (wdtype == PROX_BF16)
-    hipLaunchKernelGGL((down_kernel<Bf16Tag>), grid, dim3(kDownThreads), smem, s, a);
-  else
-    hipLaunchKernelGGL((down_kernel<F32Tag>), grid, dim3(kDownThreads), smem, s, a);
+  if (wdtype == PROX_BF16) {
+    if (from_bitmap)
+      hipLaunchKernelGGL((down_kernel<Bf16Tag, true>), grid, dim3(kDownThreads), smem, s, a);
+    else
+      hipLaunchKernelGGL((down_kernel<Bf16Tag, false>), grid, dim3(kDownThreads), smem, s, a);
+  } else {
+    if (from_bitmap)
+      hipLaunchKernelGGL((down_kernel<F32Tag, true>), grid, dim3(kDownThreads), smem, s, a);
+    else
+      hipLaunchKernelGGL((down_kernel<F32Tag, false>), grid, dim3(kDownThreads), smem, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -165,8 +165,15 @@ __global__ __launch_bounds__(kThreads) void upgate_kernel(UpGateArgs a) {
       sg = wave_sum(sg);
     }
     if (lane == 0) {
-      ssp[k0 + i] = (j >= 0) ? su * silu_f32(sg) : 0.f;
-      if (kFromBitmap) a.mask_idx[static_cast<size_t>(b) * f + k0 + i] = j;
+      const float sj = (j >= 0) ? su * silu_f32(sg) : 0.f;
+      if (kFromBitmap) {
+        // decode mode: s by channel index (the down kernel reads it through
+        // the bitmap), and the ascending index list for the caller
+        ssp[j] = sj;
+        a.mask_idx[static_cast<size_t>(b) * f + k0 + i] = j;
+      } else {
+        ssp[k0 + i] = sj;  // list mode: s by list position
+      }
     }
   }
 }

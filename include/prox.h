@@ -65,7 +65,10 @@ typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
  * One packed FFN layer.  A plain descriptor of caller-owned device buffers;
  * sizes come from prox_layer_sizes().
  *
- * proxy_q     [d_model][d_ff] bytes.  Row i holds the INT4 proxy codes of
+ * proxy_q     [d_model][qstride] bytes, qstride = d_ff when d_ff/128 is odd,
+ *             else d_ff + 128 (the last 128 bytes of a row are zero padding;
+ *             an odd multiple of 128 spreads one column slice of many rows
+ *             over the HBM channels).  Row i holds the INT4 proxy codes of
  *             input coordinate i for both W_up and W_gate, so a kept input
  *             coordinate selects one contiguous d_ff-byte run.  Within a row,
  *             each group of 16 output columns c0..c0+15 takes 16 bytes:

@@ -65,9 +65,16 @@ def oracle_view(layer: synth.Layer) -> dict:
             "x_dec": synth.as_f64(layer.x_dec, dt), "x_cal": synth.as_f64(layer.x_cal, dt)}
 
 
+def proxy_row_stride(f: int) -> int:
+    """Bytes between proxy rows, as documented in prox.h."""
+    return f if (f // 128) % 2 == 1 else f + 128
+
+
 def decode_proxy_bytes(qbytes: np.ndarray, d: int, f: int):
     """Codes of the packed proxy, read per the layout documented in prox.h."""
-    q = np.asarray(qbytes, dtype=np.uint8).reshape(d, f // 16, 2, 8)
+    rows = np.asarray(qbytes, dtype=np.uint8).reshape(d, proxy_row_stride(f))
+    assert np.all(rows[:, f:] == 0), "row padding must be zero"
+    q = rows[:, :f].reshape(d, f // 16, 2, 8)
     lo = (q & 0x0F).astype(np.int16) - 8
     hi = (q >> 4).astype(np.int16) - 8
     codes = np.empty((d, f // 16, 2, 16), dtype=np.int16)

@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol():
 def test_version_and_sizes():
     assert P.prox_abi_version() == 1
     s = P.prox_layer_sizes(4096, 12288, P.PROX_BF16)
-    assert s == (4096 * 12288, 2 * 4096 * 4, 2 * 12288 * 4096 * 2, 12288 * 4096 * 2)
+    assert s == (4096 * (12288 + 128), 2 * 4096 * 4, 2 * 12288 * 4096 * 2, 12288 * 4096 * 2)
+    assert P.prox_layer_sizes(128, 384, P.PROX_BF16)[0] == 128 * 384     # 384/128 odd: no padding
     s32 = P.prox_layer_sizes(256, 768, P.PROX_F32)
     assert s32[2] == 2 * 256 * 768 * 4
     w1 = P.prox_workspace_size(4096, 12288, 1)
