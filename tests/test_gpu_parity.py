@@ -33,11 +33,13 @@ def _small_cfg(d, f, dtype, seed, std=0.05, batch=1):
 
 
 def _bufs(P, L, b):
+    """Output buffers pre-filled with values no correct call leaves behind
+    (y is NaN, so a y that was not cleared before accumulation shows)."""
     dev = "cuda"
-    return (torch.empty(b, L.d_model, dtype=torch.float32, device=dev),
-            torch.empty(b, L.d_ff, dtype=torch.int32, device=dev),
-            torch.empty(b, dtype=torch.int32, device=dev),
-            torch.empty(b, dtype=torch.int32, device=dev))
+    return (torch.full((b, L.d_model), math.nan, dtype=torch.float32, device=dev),
+            torch.full((b, L.d_ff), -7, dtype=torch.int32, device=dev),
+            torch.full((b,), -1, dtype=torch.int32, device=dev),
+            torch.full((b,), -1, dtype=torch.int32, device=dev))
 
 
 def _oracle_taus(ov, keep_x=0.5, sparsity_s=0.7, n_tok=None):
@@ -344,6 +346,37 @@ def test_graph_replay_matches_eager(P, name):
         torch.cuda.synchronize()
         assert int(mc2.item()) == eager[rep % len(xs)][2]
     del g
+
+
+def test_decode_back_to_back_calls(P):
+    """Many stream-ordered calls on one workspace with no host synchronisation
+    in between (each call leaves the workspace ready for the next): every
+    call's outputs match the same token decoded alone."""
+    layer, ov = oracle_layer("qwen3_8b")
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov, n_tok=16)
+    toks = [0, 1, 2, 3]
+    xs = [to_device(layer.x_dec[[t]], "bf16") for t in toks]
+    ws = P.new_workspace(L.d_model, L.d_ff, 1)
+    alone = []
+    for x in xs:
+        y, mi, mc, ic = _bufs(P, L, 1)
+        P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, P.new_workspace(L.d_model, L.d_ff, 1))
+        torch.cuda.synchronize()
+        alone.append((y.cpu().numpy(), mi.cpu().numpy(), int(mc.item()), int(ic.item())))
+    n_calls = 48
+    outs = [_bufs(P, L, 1) for _ in range(n_calls)]
+    for c in range(n_calls):
+        y, mi, mc, ic = outs[c]
+        P.prox_ffn_decode(L, xs[c % len(xs)], tau_x, tau_s, y, mi, mc, ic, ws)
+    torch.cuda.synchronize()
+    for c in range(n_calls):
+        y, mi, mc, ic = outs[c]
+        ey, emi, emc, eic = alone[c % len(xs)]
+        assert int(mc.item()) == emc and int(ic.item()) == eic, f"call {c}"
+        assert np.array_equal(mi.cpu().numpy()[0, :emc], emi[0, :emc]), f"call {c}"
+        ma, rl = y_errors(y.cpu().numpy()[0], ey[0].astype(np.float64))
+        assert rl <= 1e-6, f"call {c}: rel {rl:.2e}"
 
 
 def test_decode_stages_compose(P):
