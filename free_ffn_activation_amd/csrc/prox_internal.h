@@ -13,7 +13,7 @@ namespace prox {
 // Kernel geometry (compile-time)
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 256;          // every kernel uses 4 waves of 64
-constexpr int kStage1Unroll = 8;       // proxy rows loaded per lane per batch
+constexpr int kStage1Unroll = 16;      // proxy rows loaded per lane per batch
 constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads)
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
 constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column slice

@@ -162,24 +162,26 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     acc_g[e] = 0.f;
   }
   constexpr int kWaveSlots = 64 / kLpr;
-  // Loads are unconditional (slots past the end read the sentinel) so the
-  // compiler can wait on them one at a time.
+  // One batch covers kWaveSlots * kStage1Unroll = 128 rows, a wave's whole
+  // share at 512 rows per split, so every wave makes a single round trip.
+  // Loads are unconditional (slots past the end read the sentinel row) so the
+  // compiler can wait on them one at a time; a = x_i * scale_i comes from LDS
+  // at use, and steps with no kept row in any slot are skipped.
   for (int r0 = wslot; r0 < nkept; r0 += kWaveSlots * kStage1Unroll) {
+    const int rb = r0 - wslot;  // wave-uniform base of this batch
     uint4 w[kStage1Unroll];
-    KeptA av[kStage1Unroll];
 #pragma unroll
-    for (int u = 0; u < kStage1Unroll; ++u) {
-      const int rr = min(r0 + u * kWaveSlots, nkept);
-      av[u] = ka[rr];
-      w[u] = ldg16(pbase + koff[rr]);
-    }
+    for (int u = 0; u < kStage1Unroll; ++u) w[u] = ldg16(pbase + koff[min(r0 + u * kWaveSlots, nkept)]);
     __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
 #pragma unroll
     for (int u = 0; u < kStage1Unroll; ++u) {
-      acc_dword(acc_u + 0, w[u].x, av[u].u24, av[u].u20);
-      acc_dword(acc_u + 8, w[u].y, av[u].u24, av[u].u20);
-      acc_dword(acc_g + 0, w[u].z, av[u].g24, av[u].g20);
-      acc_dword(acc_g + 8, w[u].w, av[u].g24, av[u].g20);
+      if (rb + u * kWaveSlots < nkept) {
+        const KeptA av = ka[min(r0 + u * kWaveSlots, nkept)];
+        acc_dword(acc_u + 0, w[u].x, av.u24, av.u20);
+        acc_dword(acc_u + 8, w[u].y, av.u24, av.u20);
+        acc_dword(acc_g + 0, w[u].z, av.g24, av.g20);
+        acc_dword(acc_g + 8, w[u].w, av.g24, av.g20);
+      }
     }
   }
 
