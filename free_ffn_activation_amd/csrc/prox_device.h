@@ -8,6 +8,9 @@ namespace prox {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+// 16 bytes as a native vector: whole-value copies stay in registers (copies of
+// the HIP uint4 struct can be left in private memory)
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 // Weight / activation element types.  bf16 values travel as raw 16-bit
 // patterns; fp32 as float.

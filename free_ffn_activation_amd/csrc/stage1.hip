@@ -116,25 +116,34 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   constexpr float k2p20 = 1048576.0f;
   int nkept = 0;
   float sum_up = 0.f, sum_gate = 0.f;
-  for (int base = wr0; base < wr1; base += 64) {
-    const int i = base + lane;
-    // x and both scales are fetched together (one memory round trip)
-    const int ii = min(i, wr1 - 1);
-    const float xv = load_elem<T>(a.x, static_cast<size_t>(b) * d + ii);
-    const float sc_up = a.proxy_scale[ii];
-    const float sc_gate = a.proxy_scale[d + ii];
-    const bool keep = i < wr1 && fabsf(xv) >= a.tau_x;
-    const float au = keep ? xv * sc_up : 0.f;
-    const float ag = keep ? xv * sc_gate : 0.f;
-    const uint64_t bal = __ballot(keep);
-    if (keep) {
-      const int pos = nkept + __popcll(bal & ((1ull << lane) - 1ull));
-      ka[pos] = KeptA{au * k2p24, au * k2p20, ag * k2p24, ag * k2p20};
-      koff[pos] = static_cast<uint32_t>(i) * static_cast<uint32_t>(a.proxy_stride);
+  // x and both scales of kCompactSteps 64-row steps are fetched before any is
+  // used (one memory round trip for a wave's 128 rows at 512 rows per split)
+  constexpr int kCompactSteps = 4;
+  for (int base = wr0; base < wr1; base += 64 * kCompactSteps) {
+    float xv[kCompactSteps], sc_up[kCompactSteps], sc_gate[kCompactSteps];
+#pragma unroll
+    for (int k = 0; k < kCompactSteps; ++k) {
+      const int ii = min(base + k * 64 + lane, wr1 - 1);
+      xv[k] = load_elem<T>(a.x, static_cast<size_t>(b) * d + ii);
+      sc_up[k] = a.proxy_scale[ii];
+      sc_gate[k] = a.proxy_scale[d + ii];
     }
-    nkept += __popcll(bal);
-    sum_up += au;
-    sum_gate += ag;
+#pragma unroll
+    for (int k = 0; k < kCompactSteps; ++k) {
+      const int i = base + k * 64 + lane;
+      const bool keep = i < wr1 && fabsf(xv[k]) >= a.tau_x;
+      const float au = keep ? xv[k] * sc_up[k] : 0.f;
+      const float ag = keep ? xv[k] * sc_gate[k] : 0.f;
+      const uint64_t bal = __ballot(keep);
+      if (keep) {
+        const int pos = nkept + __popcll(bal & ((1ull << lane) - 1ull));
+        ka[pos] = KeptA{au * k2p24, au * k2p20, ag * k2p24, ag * k2p20};
+        koff[pos] = static_cast<uint32_t>(i) * static_cast<uint32_t>(a.proxy_stride);
+      }
+      nkept += __popcll(bal);
+      sum_up += au;
+      sum_gate += ag;
+    }
   }
   if (lane == 0) {  // slots past the end read row 0 with weight 0
     ka[nkept] = KeptA{0.f, 0.f, 0.f, 0.f};

@@ -68,30 +68,44 @@ __global__ __launch_bounds__(kThreads) void upgate_kernel(UpGateArgs a) {
   uint4* xs = reinterpret_cast<uint4*>(smem);
   int* jl = reinterpret_cast<int*>(smem + static_cast<size_t>(nchunks) * 16);
 
-  // x -> LDS
-  const uint4* xg = reinterpret_cast<const uint4*>(static_cast<const S*>(a.x) +
-                                                   static_cast<size_t>(b) * d);
-  for (int i = tid; i < nchunks; i += kThreads) xs[i] = xg[i];
+  // Prologue loads (the bitmap words in decode mode, x) are all issued before
+  // the first wait: unconditional loads with clamped indices, then a
+  // scheduling barrier, so the prologue costs one memory round trip.
+  // Decode mode: each thread keeps a run of consecutive bitmap words in
+  // registers; one block scan of their popcounts gives every word's ordinal
+  // offset, and the thread then emits the kept channels of its own words that
+  // fall in this block's ordinal range.
+  constexpr int kXPer = (12288 / kEpl + kThreads - 1) / kThreads;  // d <= 12288
+  const u32x4_t* xg = reinterpret_cast<const u32x4_t*>(static_cast<const S*>(a.x) +
+                                                     static_cast<size_t>(b) * d);
+  u32x4_t* xsv = reinterpret_cast<u32x4_t*>(xs);
+  const int per = (nw + kThreads - 1) / kThreads;
+  const int w0 = min(nw, tid * per);
+  uint32_t wv[kMaxWordsPerThread];
+  if (kFromBitmap) {
+    const uint32_t* bm = reinterpret_cast<const uint32_t*>(
+        a.ws + static_cast<size_t>(b) * a.tok_bytes + a.off_bitmap);
+#pragma unroll
+    for (int k = 0; k < kMaxWordsPerThread; ++k) wv[k] = bm[min(w0 + k, nw - 1)];
+  }
+  u32x4_t xv[kXPer];
+#pragma unroll
+  for (int k = 0; k < kXPer; ++k) xv[k] = xg[min(tid + k * kThreads, nchunks - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  // surplus lanes rewrite the last chunk with its own value (no branch)
+#pragma unroll
+  for (int k = 0; k < kXPer; ++k) xsv[min(tid + k * kThreads, nchunks - 1)] = xv[k];
   // y is accumulated by the down kernel: clear it here
   for (int c = blockIdx.x * kThreads + tid; c < d; c += gridDim.x * kThreads)
     a.y[static_cast<size_t>(b) * d + c] = 0.f;
 
-  // Decode mode: each thread keeps a run of consecutive bitmap words in
-  // registers; one block scan of their popcounts gives every word's ordinal
-  // offset, and the thread then emits the kept channels of its own words that
-  // fall in this block's ordinal range.  One global round trip in total.
   int ks = 0;
-  uint32_t wv[kMaxWordsPerThread];
-  int w0 = 0, run = 0;
+  int run = 0;
   if (kFromBitmap) {
-    const uint32_t* bm = reinterpret_cast<const uint32_t*>(
-        a.ws + static_cast<size_t>(b) * a.tok_bytes + a.off_bitmap);
-    const int per = (nw + kThreads - 1) / kThreads;
-    w0 = min(nw, tid * per);
     int local = 0;
 #pragma unroll
     for (int k = 0; k < kMaxWordsPerThread; ++k) {
-      wv[k] = (k < per && w0 + k < nw) ? bm[w0 + k] : 0u;
+      if (!(k < per && w0 + k < nw)) wv[k] = 0u;
       local += __popc(wv[k]);
     }
     int total = 0;
