@@ -347,17 +347,18 @@ def main() -> int:
         times = []
         t_start = time.perf_counter()
         tok = 0
-        while (time.perf_counter() - t_start < args.cpu_seconds and tok < n_tok) or tok < 2:
+        # the layer's tokens in turn (repeated if needed) until about cpu_seconds
+        while time.perf_counter() - t_start < args.cpu_seconds or tok < 2:
             t1 = time.perf_counter()
-            oracle.decode(ov["x_dec"][tok], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"],
+            oracle.decode(ov["x_dec"][tok % n_tok], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"],
                           ov["qg"], ov["sg"], tx, ts)
             times.append(time.perf_counter() - t1)
             tok += 1
         threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
         cpu = {"value": round(statistics.mean(times) * 1e6, 1), "unit": "us/layer",
                "cores": int(threads), "kind": "oracle",
-               "sample": f"{len(times)} decode tokens of layer 0 ({cfg.name}, d={d}, f={f}), "
-                         f"NumPy fp64 oracle, {sum(times):.1f} s of CPU work"}
+               "sample": f"{len(times)} decode steps over the {min(len(times), n_tok)} tokens of layer 0 "
+                         f"({cfg.name}, d={d}, f={f}), NumPy fp64 oracle, {sum(times):.1f} s of CPU work"}
         log(f"CPU oracle: {cpu['value']:.0f} us/layer on {threads} threads ({len(times)} tokens)")
 
     mean_breq = sched_mean(breq)
@@ -389,7 +390,8 @@ def main() -> int:
         "dense_us_per_layer": dense,
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "traffic_detail": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
