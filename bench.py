@@ -24,6 +24,13 @@ Method of measurement
     every channel kept.
   * CPU baseline: the plain NumPy oracle on the host cores, on a bounded
     sample of tokens of layer 0.
+  * Per-step distribution (median, p10, p90) from a HIP event pair around
+    each eager step, and a 1 GiB device copy rate of the box, for context.
+  * Computation budget (the pages' budget section): alpha = Stage 1 over
+    every input / one dense bf16 projection, both timed here; the library's
+    allocator (prox_budget_s2) gives s2 for a target effective sparsity at
+    input sparsity 0.7, the layers are recalibrated and the decode is timed
+    at each such operating point (and at the pages' alpha = 1/3).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -109,6 +116,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-budget", action="store_true",
+                    help="skip the computation-budget operating points")
     ap.add_argument("--pmc-copy-mib", type=int, default=0,
                     help="only run device copies of this many MiB (counter scale reference)")
     return ap.parse_args()
@@ -152,16 +161,16 @@ def main() -> int:
     cal_ws = torch.empty(prox.prox_calibrate_workspace_size(d, f, cfg.n_cal), dtype=torch.uint8,
                          device=dev)
     x_all = torch.empty(n_layers, n_tok, d, dtype=torch.int16, device=dev)
+    x_cal = []  # kept for recalibration at other operating points
     for i, hl in enumerate(host_layers):
         L = pack_layer(hl)
         xc = to_device(hl.x_cal, cfg.dtype)
         taus.append(prox.prox_calibrate(L, xc, cfg.keep_x, sparsity, cal_ws))
         x_all[i].copy_(to_device(hl.x_dec, cfg.dtype))
         layers.append(L)
-        del xc
+        x_cal.append(xc)
     layer0_host = host_layers[0]
     del host_layers
-    del cal_ws
     torch.cuda.synchronize()
     log(f"packed {n_layers} layers ({sum(L.nbytes for L in layers) / 1e9:.2f} GB resident)")
 
@@ -212,6 +221,21 @@ def main() -> int:
     torch.cuda.synchronize()
     eager_us = (time.perf_counter() - t0) / K * 1e6
     log(f"eager: {eager_us:.2f} us/layer")
+    # per-step distribution: a HIP event pair around each eager step
+    n_ev = min(K, 640)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for s in range(n_ev):
+        evs[s][0].record()
+        step(s)
+        evs[s][1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    step_dist = {"median": round(float(np.median(per_step)), 3),
+                 "p10": round(float(np.percentile(per_step, 10)), 3),
+                 "p90": round(float(np.percentile(per_step, 90)), 3), "steps": n_ev,
+                 "timing": "eager, hipEvent pair per step"}
+    log(f"per step (eager events): median {step_dist['median']} p10 {step_dist['p10']} p90 {step_dist['p90']} us")
+    del evs
 
     # ---------------------------------------------------------------- graph timing
     def time_graph(fn, label):
@@ -335,6 +359,100 @@ def main() -> int:
             torch.cuda.synchronize()
             dense[label] = round(time_graph(fn, label)[0], 3) if not args.no_graph else None
 
+    # ---------------------------------------------------------------- box streaming context
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2.0 * nbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    log(f"device copy of 1 GiB: {copy_gbps:.0f} GB/s (read + write), for context")
+
+    # ---------------------------------------------------------------- computation budget
+    # alpha = Stage 1 over every input / one dense projection, both on this
+    # GPU; the library's allocator turns a target effective sparsity at input
+    # sparsity s1 into s2; the layers are recalibrated for (1 - s1, s2) and
+    # the decode is timed at each operating point.
+    budget = None
+    if not args.no_budget:
+        by = torch.empty(1, d, dtype=torch.float32, device=dev)
+        bmi = torch.empty(1, f, dtype=torch.int32, device=dev)
+        bmc = torch.empty(1, dtype=torch.int32, device=dev)
+        bic = torch.empty(1, dtype=torch.int32, device=dev)
+        bws = prox.new_workspace(d, f, 1)
+
+        def s1_all_inputs(s):
+            l, t = sched[s % steps_per_round]
+            prox.prox_ffn_decode_stages(layers[l], xs[l][t], 0.0, taus[l][1], by, bmi, bmc, bic, bws,
+                                        prox.PROX_STAGE_PROXY)
+
+        t_s1_all = time_graph(s1_all_inputs, "stage 1 over every input")[0]
+        wug2 = [L.w_upgate_t.view(torch.bfloat16).view(2 * f, d) for L in layers]
+        xb2 = [[xs[l][t].view(torch.bfloat16) for t in range(n_tok)] for l in range(n_layers)]
+
+        def torch_two_projections(s):
+            l, t = sched[s % steps_per_round]
+            torch.nn.functional.linear(xb2[l][t], wug2[l])
+
+        all_j2 = torch.arange(f, dtype=torch.int32, device=dev).view(1, f)
+        all_c2 = torch.full((1,), f, dtype=torch.int32, device=dev)
+
+        def own_three_projections(s):
+            l, t = sched[s % steps_per_round]
+            prox.prox_ffn_stage2(layers[l], xs[l][t], all_j2, all_c2, by, bws)
+
+        t_proj_torch = time_graph(torch_two_projections, "torch bf16 up+gate projections")[0] / 2
+        t_proj_own = time_graph(own_three_projections, "own dense Stage 2 (3 projections)")[0] / 3
+        t_proj = min(t_proj_torch, t_proj_own)
+        alpha = t_s1_all / t_proj
+        log(f"alpha = {t_s1_all:.2f} / {t_proj:.2f} = {alpha:.3f}")
+        cal_keep = []
+        points = [("pages' alpha", 0.7, 0.7, 1.0 / 3.0)] + [("measured alpha", e, 0.7, alpha) for e in (0.5, 0.6, 0.7)]
+        op_out = []
+        for label, e_t, s1, a in points:
+            try:
+                s2 = prox.prox_budget_s2(e_t, s1, a)
+            except prox.ProxError as exc:
+                op_out.append({"alpha_from": label, "e_target": e_t, "s1": s1, "alpha": round(a, 4),
+                               "reachable": False, "reason": str(exc)})
+                continue
+            taus_op = [prox.prox_calibrate(layers[l], x_cal[l], 1.0 - s1, s2, cal_ws) for l in range(n_layers)]
+            kx_o = np.zeros((n_layers, n_tok), np.int64)
+            ks_o = np.zeros((n_layers, n_tok), np.int64)
+            for l in range(n_layers):
+                for t in range(n_tok):
+                    prox.prox_ffn_decode(layers[l], xs[l][t], taus_op[l][0], taus_op[l][1], by, bmi, bmc, bic, bws)
+                    torch.cuda.synchronize()
+                    kx_o[l, t], ks_o[l, t] = int(bic.item()), int(bmc.item())
+            breq_o = kx_o * f + 8 * kx_o + 3 * ks_o * d * w + d * w + 4 * d + 4 * ks_o
+
+            def step_op(s, taus_op=taus_op):
+                l, t = sched[s % steps_per_round]
+                prox.prox_ffn_decode(layers[l], xs[l][t], taus_op[l][0], taus_op[l][1], by, bmi, bmc, bic, bws)
+
+            us_o = time_graph(step_op, f"decode at e={e_t} s1={s1} s2={s2:.4f} ({label})")[0]
+            mb = sched_mean(breq_o)
+            keep_x_run, keep_s_run = sched_mean(kx_o) / d, sched_mean(ks_o) / f
+            op_out.append({"alpha_from": label, "e_target": e_t, "s1": s1, "s2": round(s2, 4),
+                           "alpha": round(a, 4), "reachable": True, "us_per_layer": round(us_o, 3),
+                           "required_MB": round(mb / 1e6, 3), "GBps": round(mb / (us_o * 1e-6) / 1e9, 1),
+                           "pct_hbm_roofline": round(100.0 * mb / (us_o * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                           "runtime_keep_x": round(keep_x_run, 4), "runtime_keep_s": round(keep_s_run, 4),
+                           "runtime_effective_sparsity": round(
+                               prox.prox_budget_effective(1.0 - keep_x_run, 1.0 - keep_s_run, a), 4)})
+        budget = {"alpha": round(alpha, 4), "t_stage1_all_inputs_us": round(t_s1_all, 3),
+                  "t_dense_projection_us": round(t_proj, 3),
+                  "t_dense_projection_torch_us": round(t_proj_torch, 3),
+                  "t_dense_projection_own_us": round(t_proj_own, 3), "operating_points": op_out}
+        del bws, wug2, xb2
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -386,6 +504,8 @@ def main() -> int:
         "mean_k_x": round(sched_mean(kx), 1),
         "mean_k_s": round(sched_mean(ksv), 1),
         "eager_us_per_layer": round(eager_us, 3),
+        "step_us": step_dist,
+        "box_copy_GBps_read_plus_write": round(copy_gbps, 1),
         "kernels": kernels,
         "dense_us_per_layer": dense,
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(ach, 1),
@@ -393,6 +513,7 @@ def main() -> int:
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "traffic_detail": traffic},
         "cpu_baseline": cpu,
+        "budget": budget,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -371,6 +371,39 @@ PROX_API prox_status prox_calibrate_workspace_size(int32_t d, int32_t f, int32_t
   }
 }
 
+namespace {
+prox_status check_budget_args(float a, float b, float alpha) {
+  if (!(a >= 0.f && a <= 1.f) || !(b >= 0.f && b <= 1.f))
+    return fail(PROX_ERR_INVALID_ARG, "sparsities must lie in [0, 1]");
+  if (!(alpha > 0.f) || std::isinf(alpha))
+    return fail(PROX_ERR_INVALID_ARG, "alpha = %g must be finite and > 0", static_cast<double>(alpha));
+  return PROX_OK;
+}
+}  // namespace
+
+PROX_API prox_status prox_budget_effective(float s1, float s2, float alpha, float* e_out) {
+  g_err.clear();
+  if (!e_out) return fail(PROX_ERR_INVALID_ARG, "e_out is NULL");
+  const prox_status st = check_budget_args(s1, s2, alpha);
+  if (st != PROX_OK) return st;
+  const double cost = 2.0 * alpha * (1.0 - static_cast<double>(s1)) + 3.0 * (1.0 - static_cast<double>(s2));
+  *e_out = static_cast<float>(1.0 - cost / 3.0);
+  return PROX_OK;
+}
+
+PROX_API prox_status prox_budget_s2(float e_target, float s1, float alpha, float* s2_out) {
+  g_err.clear();
+  if (!s2_out) return fail(PROX_ERR_INVALID_ARG, "s2_out is NULL");
+  const prox_status st = check_budget_args(e_target, s1, alpha);
+  if (st != PROX_OK) return st;
+  const double s2 = static_cast<double>(e_target) + 2.0 * alpha * (1.0 - static_cast<double>(s1)) / 3.0;
+  if (s2 > 1.0)
+    return fail(PROX_ERR_UNSUPPORTED, "effective sparsity %g is out of reach at s1 = %g, alpha = %g (needs s2 = %g)",
+                static_cast<double>(e_target), static_cast<double>(s1), static_cast<double>(alpha), s2);
+  *s2_out = static_cast<float>(s2);
+  return PROX_OK;
+}
+
 PROX_API prox_status prox_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   try {
     g_err.clear();

@@ -31,7 +31,8 @@ _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPO
                  -3: "PROX_ERR_HIP", -4: "PROX_ERR_INTERNAL"}
 
 EXPORTED = ("prox_abi_version", "prox_last_error", "prox_layer_sizes", "prox_workspace_size",
-            "prox_calibrate_workspace_size", "prox_workspace_init", "prox_pack_proxy",
+            "prox_calibrate_workspace_size", "prox_budget_effective", "prox_budget_s2",
+            "prox_workspace_init", "prox_pack_proxy",
             "prox_calibrate", "prox_ffn_decode", "prox_ffn_decode_events",
             "prox_ffn_decode_stages", "prox_ffn_stage2", "prox_proxy_state")
 
@@ -62,6 +63,8 @@ _sig = {
     "prox_last_error": (ctypes.c_char_p, []),
     "prox_layer_sizes": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
     "prox_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
+    "prox_budget_effective": (_c_i32, [_c_f32, _c_f32, _c_f32, _P(_c_f32)]),
+    "prox_budget_s2": (_c_i32, [_c_f32, _c_f32, _c_f32, _P(_c_f32)]),
     "prox_calibrate_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
     "prox_workspace_init": (_c_i32, [_c_vp, _c_size, _c_vp]),
     "prox_pack_proxy": (_c_i32, [_c_vp, _c_vp, _c_vp, _P(prox_layer), _c_vp]),
@@ -126,6 +129,18 @@ def prox_abi_version() -> int:
 
 def prox_last_error() -> str:
     return _lib.prox_last_error().decode("utf-8", "replace")
+
+
+def prox_budget_effective(s1: float, s2: float, alpha: float) -> float:
+    out = _c_f32(0.0)
+    _check(_lib.prox_budget_effective(s1, s2, alpha, ctypes.byref(out)))
+    return float(out.value)
+
+
+def prox_budget_s2(e_target: float, s1: float, alpha: float) -> float:
+    out = _c_f32(0.0)
+    _check(_lib.prox_budget_s2(e_target, s1, alpha, ctypes.byref(out)))
+    return float(out.value)
 
 
 def prox_layer_sizes(d_model: int, d_ff: int, wdtype: int) -> tuple:

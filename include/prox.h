@@ -113,6 +113,26 @@ prox_status prox_workspace_size(int32_t d_model, int32_t d_ff, int32_t batch, si
 prox_status prox_calibrate_workspace_size(int32_t d_model, int32_t d_ff, int32_t n_tokens,
                                           size_t* bytes);
 
+/*
+ * Computation-budget allocator ([blog] computation-budget section).  With the
+ * dense FFN counted as 3 units (up, gate, down), Stage 1 costs
+ * 2 * alpha * (1 - s1) units and Stage 2 costs 3 * (1 - s2), where s1 is the
+ * input sparsity (1 - keep_x), s2 the channel sparsity and alpha the time of
+ * the INT4 proxy pass over every input (both proxies) divided by the time of
+ * one dense projection, measured on the target GPU.  The effective sparsity
+ * is e = 1 - cost / 3 = s2 - 2 * alpha * (1 - s1) / 3.  Host arithmetic in
+ * double; no GPU work; outputs are host floats.
+ *   prox_budget_effective: e for (s1, s2, alpha).
+ *   prox_budget_s2: the s2 that reaches e_target at s1:
+ *     s2 = e_target + 2 * alpha * (1 - s1) / 3; PROX_ERR_UNSUPPORTED (and
+ *     *s2_out untouched) when that exceeds 1, i.e. the target is out of reach
+ *     at this s1.
+ * Arguments: s1, s2, e_target in [0, 1]; alpha finite and > 0; else
+ * PROX_ERR_INVALID_ARG.
+ */
+prox_status prox_budget_effective(float s1, float s2, float alpha, float* e_out);
+prox_status prox_budget_s2(float e_target, float s1, float alpha, float* s2_out);
+
 /* Zero a workspace (device, ws_bytes) on `stream`.  A decode workspace must be
  * zeroed once before its first use (this call or any zero fill); every
  * completed call leaves it ready for the next one. */
