@@ -453,6 +453,39 @@ def main() -> int:
                   "t_dense_projection_own_us": round(t_proj_own, 3), "operating_points": op_out}
         del bws, wug2, xb2
 
+    # ---------------------------------------------------------------- GeGLU layers
+    # the same packed layers read as GeGLU (GELU-tanh gate), recalibrated at the
+    # headline keep / sparsity, timed over the same rotation
+    geglu = None
+    if not args.no_budget:
+        layers_g = [L.with_activation(prox.PROX_ACT_GELU_TANH) for L in layers]
+        taus_g = [prox.prox_calibrate(layers_g[l], x_cal[l], cfg.keep_x, sparsity, cal_ws)
+                  for l in range(n_layers)]
+        gy = torch.empty(1, d, dtype=torch.float32, device=dev)
+        gmi = torch.empty(1, f, dtype=torch.int32, device=dev)
+        gmc = torch.empty(1, dtype=torch.int32, device=dev)
+        gic = torch.empty(1, dtype=torch.int32, device=dev)
+        gws = prox.new_workspace(d, f, 1)
+        kx_g = np.zeros((n_layers, n_tok), np.int64)
+        ks_g = np.zeros((n_layers, n_tok), np.int64)
+        for l in range(n_layers):
+            for t in range(n_tok):
+                prox.prox_ffn_decode(layers_g[l], xs[l][t], taus_g[l][0], taus_g[l][1], gy, gmi, gmc, gic, gws)
+                torch.cuda.synchronize()
+                kx_g[l, t], ks_g[l, t] = int(gic.item()), int(gmc.item())
+
+        def step_g(s):
+            l, t = sched[s % steps_per_round]
+            prox.prox_ffn_decode(layers_g[l], xs[l][t], taus_g[l][0], taus_g[l][1], gy, gmi, gmc, gic, gws)
+
+        us_g = time_graph(step_g, "GeGLU decode")[0]
+        mb_g = sched_mean(kx_g * f + 8 * kx_g + 3 * ks_g * d * w + d * w + 4 * d + 4 * ks_g)
+        geglu = {"activation": "gelu_tanh", "us_per_layer": round(us_g, 3), "required_MB": round(mb_g / 1e6, 3),
+                 "GBps": round(mb_g / (us_g * 1e-6) / 1e9, 1),
+                 "pct_hbm_roofline": round(100.0 * mb_g / (us_g * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                 "mean_k_x": round(sched_mean(kx_g), 1), "mean_k_s": round(sched_mean(ks_g), 1)}
+        del gws
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -514,6 +547,7 @@ def main() -> int:
                      "traffic_detail": traffic},
         "cpu_baseline": cpu,
         "budget": budget,
+        "geglu": geglu,
     }
     print(json.dumps(out), flush=True)
     return 0

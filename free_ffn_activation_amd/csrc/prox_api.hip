@@ -54,7 +54,9 @@ prox_status check_layer(const prox_layer* L) {
   if (L == nullptr) return fail(PROX_ERR_INVALID_ARG, "layer descriptor is NULL");
   prox_status st = check_shape(L->d_model, L->d_ff, L->wdtype);
   if (st != PROX_OK) return st;
-  if (L->reserved != 0) return fail(PROX_ERR_INVALID_ARG, "layer->reserved must be 0");
+  if (L->activation != PROX_ACT_SILU && L->activation != PROX_ACT_GELU_TANH)
+    return fail(PROX_ERR_INVALID_ARG, "layer->activation %d is neither PROX_ACT_SILU nor PROX_ACT_GELU_TANH",
+                L->activation);
   if (!L->proxy_q || !L->proxy_scale || !L->w_upgate_t || !L->w_down)
     return fail(PROX_ERR_INVALID_ARG, "layer buffer pointer is NULL");
   if (!aligned(L->proxy_q, 16) || !aligned(L->proxy_scale, 16) || !aligned(L->w_upgate_t, 16) ||
@@ -108,6 +110,7 @@ Stage1Args stage1_args(const Plan& p, const prox_layer* L, const void* x, float 
   a.off_bitmap = p.off_bitmap;
   a.s_tilde = s_tilde;
   a.in_count = in_count;
+  a.act = L->activation;
   return a;
 }
 
@@ -117,6 +120,7 @@ UpGateArgs upgate_args(const Plan& p, const prox_layer* L, const void* x, void* 
   a.d = p.d;
   a.f = p.f;
   a.max_cpb = p.ug_max_cpb;
+  a.act = L->activation;
   a.w_upgate_t = L->w_upgate_t;
   a.x = x;
   a.ws = static_cast<const uint8_t*>(ws);

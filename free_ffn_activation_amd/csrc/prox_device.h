@@ -76,4 +76,15 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 // SiLU(z) = z / (1 + e^{-z}); e^{-z} overflowing to +inf gives -0 as required.
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
+// GELU in its tanh form, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+__device__ __forceinline__ float gelu_tanh_f32(float z) {
+  const float k = 0.7978845608028654f;  // sqrt(2 / pi)
+  return 0.5f * z * (1.0f + tanhf(k * (z + 0.044715f * z * z * z)));
+}
+
+// The layer's gate non-linearity (prox_activation); `act` is uniform.
+__device__ __forceinline__ float gate_act(float z, int act) {
+  return act == 1 ? gelu_tanh_f32(z) : silu_f32(z);
+}
+
 }  // namespace prox

@@ -54,10 +54,12 @@ struct Stage1Args {
   size_t tok_bytes, off_tickets, off_kcount, off_partial, off_bitmap;
   float* s_tilde;         // [batch][f] or nullptr
   int* in_count;          // [batch] or nullptr
+  int act;                // prox_activation
 };
 
 struct UpGateArgs {
   int d, f, max_cpb;
+  int act;                // prox_activation
   const void* w_upgate_t; // [f][2][d]
   const void* x;          // [batch][d]
   const uint8_t* ws;      // bitmap source (decode mode)

@@ -3,7 +3,8 @@
 //
 // Method ([blog] = deep-dive blog "Prox 完全拆解", section "Stage 1"):
 //   m_x = 1[|x_i| >= tau_x];  u~ = Pi^in(x, W~_up, m_x);
-//   h~ = SiLU(Pi^in(x, W~_gate, m_x));  s~ = u~ * h~;  m_s = 1[|s~_j| >= tau_s].
+//   h~ = SiLU(Pi^in(x, W~_gate, m_x));  s~ = u~ * h~;  m_s = 1[|s~_j| >= tau_s]
+// (GELU in place of SiLU for a GeGLU layer: the layer's activation field).
 // The pages' kernel ([blog] section on turning the formulas into GPU work) is
 // a fused split-N kernel that shares one read of the hidden state between
 // the up and gate proxies, skips rejected inputs inside the main loop, unpacks
@@ -30,7 +31,7 @@
 //     row sums are corrected by 8 * sum(a) once per block.
 //   * the K-split partial sums go to the workspace; a self-resetting ticket
 //     per panel lets the last block add them in fixed split order (so masks
-//     are run-to-run identical), apply SiLU, ballot |s~| >= tau_s and write
+//     are run-to-run identical), apply the gate activation, ballot |s~| >= tau_s and write
 //     the panel's 128 mask bits.
 //   * hand-off between blocks without cache-wide maintenance: the partials
 //     are written with device-scope stores (sc1: written through to the point
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     __hip_atomic_store(&kcount[split], s_wave_cnt[0] + s_wave_cnt[1] + s_wave_cnt[2] + s_wave_cnt[3],
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- last block of this panel: fixed-order sum of the splits, SiLU, mask
+  // ---- last block of this panel: fixed-order sum of the splits, activation, mask
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are complete
   __syncthreads();
   if (tid == 0) {
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   for (int c = tid; c < kPw; c += kThreads) {  // wave-uniform trip count
     const float uu = sv[c];
     const float gg = sv[kPw + c];
-    const float st = uu * silu_f32(gg);
+    const float st = uu * gate_act(gg, a.act);
     const size_t gc = static_cast<size_t>(panel) * kPw + c;
     if (kWriteState) a.s_tilde[static_cast<size_t>(b) * f + gc] = st;
     const uint64_t bal = __ballot(fabsf(st) >= a.tau_s);

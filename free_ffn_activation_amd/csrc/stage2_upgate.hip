@@ -3,7 +3,8 @@
 //
 // Method ([blog] = deep-dive blog "Prox 完全拆解", section "Stage 2"):
 //   u_sp = Pi^out(x, W_up, m_s), h_sp = SiLU(Pi^out(x, W_gate, m_s)),
-//   s_sp = u_sp * h_sp, with the dense x and the original weights.
+//   s_sp = u_sp * h_sp, with the dense x and the original weights (GELU in
+//   place of SiLU for a GeGLU layer).
 // The pages fuse the output-sparse up and gate projections into one kernel
 // ([blog] section on turning the formulas into GPU work).
 //
@@ -18,7 +19,7 @@
 //   * one wave per channel: 64 lanes x 16 B per load cover 512 bf16 of a run;
 //     up to 8 steps (16 loads, 16 KB per wave) are issued before use.  x lives
 //     in LDS.  bf16 products use v_dot2_f32_bf16 (exact products, fp32 sum).
-//   * a wave reduction gives u_j and g_j; lane 0 stores s_j = u_j SiLU(g_j).
+//   * a wave reduction gives u_j and g_j; lane 0 stores s_j = u_j act(g_j).
 //   * this kernel also zeroes y, which the down kernel accumulates into.
 #include "prox_device.h"
 #include "prox_internal.h"
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void upgate_kernel(UpGateArgs a) {
       sg = wave_sum(sg);
     }
     if (lane == 0) {
-      const float sj = (j >= 0) ? su * silu_f32(sg) : 0.f;
+      const float sj = (j >= 0) ? su * gate_act(sg, a.act) : 0.f;
       if (kFromBitmap) {
         // decode mode: s by channel index (the down kernel reads it through
         // the bitmap), and the ascending index list for the caller

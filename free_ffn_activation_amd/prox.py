@@ -23,6 +23,8 @@ PROX_ERR_HIP = -3
 PROX_ERR_INTERNAL = -4
 PROX_F32 = 0
 PROX_BF16 = 1
+PROX_ACT_SILU = 0
+PROX_ACT_GELU_TANH = 1
 PROX_STAGE_PROXY = 1
 PROX_STAGE_UPGATE = 2
 PROX_STAGE_DOWN = 4
@@ -52,7 +54,7 @@ _c_i32, _c_f32, _c_size, _c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 
 
 class prox_layer(ctypes.Structure):
-    _fields_ = [("d_model", _c_i32), ("d_ff", _c_i32), ("wdtype", _c_i32), ("reserved", _c_i32),
+    _fields_ = [("d_model", _c_i32), ("d_ff", _c_i32), ("wdtype", _c_i32), ("activation", _c_i32),
                 ("proxy_q", _c_vp), ("proxy_scale", _c_vp), ("w_upgate_t", _c_vp),
                 ("w_down", _c_vp)]
 
@@ -166,18 +168,29 @@ class ProxLayer:
     """Device buffers of one packed layer (allocated by torch) and their
     prox_layer descriptor."""
 
-    def __init__(self, d_model: int, d_ff: int, wdtype: int, device="cuda"):
+    def __init__(self, d_model: int, d_ff: int, wdtype: int, device="cuda", activation: int = 0):
         sizes = prox_layer_sizes(d_model, d_ff, wdtype)
-        self.d_model, self.d_ff, self.wdtype = d_model, d_ff, wdtype
+        self.d_model, self.d_ff, self.wdtype, self.activation = d_model, d_ff, wdtype, activation
         wt = torch.float32 if wdtype == PROX_F32 else torch.int16
         es = 4 if wdtype == PROX_F32 else 2
         self.proxy_q = torch.empty(sizes[0], dtype=torch.uint8, device=device)
         self.proxy_scale = torch.empty(sizes[1] // 4, dtype=torch.float32, device=device)
         self.w_upgate_t = torch.empty(sizes[2] // es, dtype=wt, device=device)
         self.w_down = torch.empty(sizes[3] // es, dtype=wt, device=device)
-        self.desc = prox_layer(d_model, d_ff, wdtype, 0, self.proxy_q.data_ptr(),
+        self.desc = prox_layer(d_model, d_ff, wdtype, activation, self.proxy_q.data_ptr(),
                                self.proxy_scale.data_ptr(), self.w_upgate_t.data_ptr(),
                                self.w_down.data_ptr())
+
+    def with_activation(self, activation: int) -> "ProxLayer":
+        """Another descriptor over the same packed buffers with a different gate
+        activation (the packed data does not depend on it)."""
+        other = object.__new__(ProxLayer)
+        other.__dict__.update(self.__dict__)
+        other.activation = activation
+        other.desc = prox_layer(self.d_model, self.d_ff, self.wdtype, activation, self.proxy_q.data_ptr(),
+                                self.proxy_scale.data_ptr(), self.w_upgate_t.data_ptr(),
+                                self.w_down.data_ptr())
+        return other
 
     @property
     def nbytes(self) -> int:

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PROX_ABI_VERSION 1
+#define PROX_ABI_VERSION 2
 
 typedef enum {
   PROX_OK = 0,
@@ -81,12 +81,20 @@ typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
  * w_upgate_t  [d_ff][2][d_model] in wdtype: for channel j, W_up[:, j] then
  *             W_gate[:, j], each a contiguous d_model-long run.
  * w_down      [d_ff][d_model] in wdtype, row-major (row j = W_down[j, :]).
+ * activation  the gate non-linearity of the FFN, used in the proxy state and
+ *             in Stage 2 alike: PROX_ACT_SILU (SwiGLU, SiLU(z) = z/(1+e^-z)) or
+ *             PROX_ACT_GELU_TANH (GeGLU, Gemma-3 style: GELU in its tanh form
+ *             0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))).  The pages
+ *             evaluate the method on SwiGLU models and on GeGLU-style Gemma-3
+ *             ([blog] evidence section).
  */
+typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
+
 typedef struct {
   int32_t d_model;
   int32_t d_ff;
-  int32_t wdtype;   /* prox_dtype */
-  int32_t reserved; /* must be 0 */
+  int32_t wdtype;     /* prox_dtype */
+  int32_t activation; /* prox_activation */
   void* proxy_q;
   float* proxy_scale;
   void* w_upgate_t;

@@ -31,6 +31,10 @@ Readings where the pages are silent (each also listed in the design notes):
   R10 SiLU(z) = z / (1 + exp(-z)).
   R13 empty masks give zero output.
   R14 index lists are ascending.
+  R18 GeGLU layers (the pages evaluate GeGLU-style Gemma-3 as well as SwiGLU
+      models) use GELU in its tanh form,
+      0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), in both the proxy
+      state and Stage 2; everything else is unchanged.
 
 Parity pins: every function here is pinned by tests that do not route through
 itself (dense SwiGLU, brute-force sorts, closed forms, page values); the
@@ -52,6 +56,17 @@ def silu(z: np.ndarray) -> np.ndarray:
     z = np.asarray(z, dtype=np.float64)
     with np.errstate(over="ignore"):
         return z / (1.0 + np.exp(-z))
+
+
+def gelu_tanh(z: np.ndarray) -> np.ndarray:
+    """GELU in its tanh form (reading R18), the gate non-linearity of a GeGLU
+    FFN.  [blog] evidence section: GeGLU-style Gemma-3 is among the models the
+    method is evaluated on, with the gate activation in place of SiLU."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+ACTIVATIONS = {"silu": silu, "gelu_tanh": gelu_tanh}
 
 
 def index_set(m: np.ndarray) -> np.ndarray:
@@ -110,12 +125,13 @@ def input_mask(x: np.ndarray, tau_x: float) -> np.ndarray:
     return np.abs(np.asarray(x, dtype=np.float64)) >= np.float64(tau_x)
 
 
-def proxy_state(x, q_up, sc_up, q_gate, sc_gate, tau_x):
+def proxy_state(x, q_up, sc_up, q_gate, sc_gate, tau_x, act="silu"):
     """Stage-1 proxy state for one token.
 
     [blog] section "Stage 1": u~ = Pi^in(x, W~_up, m_x),
     h~ = SiLU(Pi^in(x, W~_gate, m_x)), s~ = u~ * h~, with one input mask shared
-    by both branches.  Returns dict(u, g, s, m_x).
+    by both branches (GELU in place of SiLU for a GeGLU layer, R18).
+    Returns dict(u, g, s, m_x).
     """
     x = np.asarray(x, dtype=np.float64)
     m_x = input_mask(x, tau_x)
@@ -124,7 +140,7 @@ def proxy_state(x, q_up, sc_up, q_gate, sc_gate, tau_x):
     # dequantised: W~[I, :] = diag(scale[I]) q[I, :].
     u = x[idx] @ dequantize(q_up[idx], sc_up[idx])
     g = x[idx] @ dequantize(q_gate[idx], sc_gate[idx])
-    s = u * silu(g)
+    s = u * ACTIVATIONS[act](g)
     return {"u": u, "g": g, "s": s, "m_x": m_x}
 
 
@@ -136,8 +152,9 @@ def channel_mask(s_tilde: np.ndarray, tau_s: float) -> np.ndarray:
 # --------------------------------------------------------------------------
 # O5-O6: Stage 2, exact compute on the kept channels
 # --------------------------------------------------------------------------
-def stage2(x, W_up, W_gate, W_down, m_s):
-    """Exact sparse SwiGLU on the channels of m_s.
+def stage2(x, W_up, W_gate, W_down, m_s, act="silu"):
+    """Exact sparse SwiGLU (GeGLU with act="gelu_tanh", R18) on the channels
+    of m_s.
 
     [blog] section "Stage 2": u_sp = Pi^out(x, W_up, m_s),
     h_sp = SiLU(Pi^out(x, W_gate, m_s)), s_sp = u_sp * h_sp,
@@ -147,7 +164,7 @@ def stage2(x, W_up, W_gate, W_down, m_s):
     x = np.asarray(x, dtype=np.float64)
     u_sp = pi_out(x, W_up, m_s)
     g_sp = pi_out(x, W_gate, m_s)
-    h_sp = silu(g_sp)
+    h_sp = ACTIVATIONS[act](g_sp)
     s_sp = u_sp * h_sp
     # Pi^in over the kept rows of W_down; s_sp is already restricted to I(m_s),
     # so scatter it back to a full-length vector before applying the definition.
@@ -160,7 +177,7 @@ def stage2(x, W_up, W_gate, W_down, m_s):
 # --------------------------------------------------------------------------
 # Whole decode step
 # --------------------------------------------------------------------------
-def decode(x, W_up, W_gate, W_down, q_up, sc_up, q_gate, sc_gate, tau_x, tau_s):
+def decode(x, W_up, W_gate, W_down, q_up, sc_up, q_gate, sc_gate, tau_x, tau_s, act="silu"):
     """One Prox FFN decode step for one token (batch rows run independently).
 
     Stage 1 ([blog] "Stage 1") produces the shared channel mask from the INT4
@@ -169,9 +186,9 @@ def decode(x, W_up, W_gate, W_down, q_up, sc_up, q_gate, sc_gate, tau_x, tau_s):
     the mask boundary).
     Returns dict(y, J (ascending int64), k_x, k_s, s_tilde, m_x, m_s, s_sp).
     """
-    st = proxy_state(x, q_up, sc_up, q_gate, sc_gate, tau_x)
+    st = proxy_state(x, q_up, sc_up, q_gate, sc_gate, tau_x, act)
     m_s = channel_mask(st["s"], tau_s)
-    out = stage2(x, W_up, W_gate, W_down, m_s)
+    out = stage2(x, W_up, W_gate, W_down, m_s, act)
     return {"y": out["y"], "J": index_set(m_s), "k_x": int(st["m_x"].sum()),
             "k_s": int(m_s.sum()), "s_tilde": st["s"], "m_x": st["m_x"], "m_s": m_s,
             "s_sp": out["s"]}
@@ -195,7 +212,7 @@ def order_statistic_keep(values: np.ndarray, keep: int) -> float:
     return float(v[v.size - keep])
 
 
-def calibrate(X_cal, q_up, sc_up, q_gate, sc_gate, keep_x: float, sparsity_s: float):
+def calibrate(X_cal, q_up, sc_up, q_gate, sc_gate, keep_x: float, sparsity_s: float, act="silu"):
     """Per-layer thresholds (tau_x, tau_s) from calibration tokens.
 
     [blog] "evidence" section (calibration paragraph): fixed per-layer scalar
@@ -209,7 +226,7 @@ def calibrate(X_cal, q_up, sc_up, q_gate, sc_gate, keep_x: float, sparsity_s: fl
     tau_x = order_statistic_keep(ax, n_keep(float(keep_x), ax.size))
     tau_x32 = float(np.float32(tau_x)) if math.isfinite(tau_x) else math.inf
     s_all = np.concatenate([
-        np.abs(proxy_state(X[t], q_up, sc_up, q_gate, sc_gate, tau_x32)["s"])
+        np.abs(proxy_state(X[t], q_up, sc_up, q_gate, sc_gate, tau_x32, act)["s"])
         for t in range(X.shape[0])])
     keep_s = 1.0 - float(np.float32(sparsity_s))
     tau_s = order_statistic_keep(s_all, n_keep(keep_s, s_all.size))

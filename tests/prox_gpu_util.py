@@ -32,11 +32,13 @@ def wdtype_code(dtype: str) -> int:
     return prox.PROX_BF16 if dtype == "bf16" else prox.PROX_F32
 
 
-def pack_layer(layer: synth.Layer, device="cuda"):
-    """Upload W_up/W_gate/W_down and run prox_pack_proxy.  Returns ProxLayer."""
+def pack_layer(layer: synth.Layer, device="cuda", activation: int = 0):
+    """Upload W_up/W_gate/W_down and run prox_pack_proxy.  Returns ProxLayer
+    (activation: 0 SiLU / SwiGLU, 1 GELU-tanh / GeGLU)."""
     from free_ffn_activation_amd import prox
     cfg = layer.cfg
-    L = prox.ProxLayer(cfg.d_model, cfg.d_ff, wdtype_code(cfg.dtype), device=device)
+    L = prox.ProxLayer(cfg.d_model, cfg.d_ff, wdtype_code(cfg.dtype), device=device,
+                       activation=activation)
     wu = to_device(layer.w_up, cfg.dtype, device)
     wg = to_device(layer.w_gate, cfg.dtype, device)
     wd = to_device(layer.w_down, cfg.dtype, device)

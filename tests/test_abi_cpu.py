@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_sizes():
-    assert P.prox_abi_version() == 1
+    assert P.prox_abi_version() == 2
     s = P.prox_layer_sizes(4096, 12288, P.PROX_BF16)
     assert s == (4096 * (12288 + 128), 2 * 4096 * 4, 2 * 12288 * 4096 * 2, 12288 * 4096 * 2)
     assert P.prox_layer_sizes(128, 384, P.PROX_BF16)[0] == 128 * 384     # 384/128 odd: no padding
@@ -80,7 +80,7 @@ def test_decode_argument_validation():
     ok_layer = _layer()
     assert _decode(None) == P.PROX_ERR_INVALID_ARG
     assert _decode(_layer(proxy_q=None)) == P.PROX_ERR_INVALID_ARG
-    assert _decode(_layer(reserved=1)) == P.PROX_ERR_INVALID_ARG
+    assert _decode(_layer(activation=2)) == P.PROX_ERR_INVALID_ARG
     assert _decode(_layer(d=250)) == P.PROX_ERR_UNSUPPORTED
     assert _decode(_layer(w_down=FAKE + 8)) == P.PROX_ERR_INVALID_ARG     # misaligned
     assert _decode(ok_layer, batch=0) == P.PROX_ERR_INVALID_ARG

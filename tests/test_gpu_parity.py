@@ -42,12 +42,12 @@ def _bufs(P, L, b):
             torch.full((b,), -1, dtype=torch.int32, device=dev))
 
 
-def _oracle_taus(ov, keep_x=0.5, sparsity_s=0.7, n_tok=None):
+def _oracle_taus(ov, keep_x=0.5, sparsity_s=0.7, n_tok=None, act="silu"):
     xc = ov["x_cal"] if n_tok is None else ov["x_cal"][:n_tok]
-    return oracle.calibrate(xc, ov["qu"], ov["su"], ov["qg"], ov["sg"], keep_x, sparsity_s)
+    return oracle.calibrate(xc, ov["qu"], ov["su"], ov["qg"], ov["sg"], keep_x, sparsity_s, act=act)
 
 
-def _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, label):
+def _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, label, act="silu"):
     dt = layer.cfg.dtype
     x = to_device(layer.x_dec[tokens], dt)
     b = len(tokens)
@@ -59,7 +59,7 @@ def _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, label):
     total_band = 0
     for k, t in enumerate(tokens):
         ref = oracle.decode(ov["x_dec"][t], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"],
-                            ov["qg"], ov["sg"], tau_x, tau_s)
+                            ov["qg"], ov["sg"], tau_x, tau_s, act=act)
         assert ic[k] == ref["k_x"], f"{label} token {t}: k_x {ic[k]} != {ref['k_x']}"
         oob, inb, asc = band_compare(mi[k], int(mc[k]), ref["s_tilde"], tau_s)
         assert asc, f"{label} token {t}: index list not ascending / in range"
@@ -68,7 +68,7 @@ def _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, label):
         # y against the oracle's Stage 2 on the GPU's own channel list
         m_gpu = np.zeros(L.d_ff, bool)
         m_gpu[mi[k][: mc[k]]] = True
-        y_ref = oracle.stage2(ov["x_dec"][t], ov["Wu"], ov["Wg"], ov["Wd"], m_gpu)["y"]
+        y_ref = oracle.stage2(ov["x_dec"][t], ov["Wu"], ov["Wg"], ov["Wd"], m_gpu, act=act)["y"]
         if not m_gpu.any():
             assert np.all(y[k] == 0.0)
         else:
@@ -403,3 +403,53 @@ def test_decode_stages_compose(P):
     P.prox_ffn_decode_stages(L, x, tau_x, tau_s, y2, mi2, mc2, ic2, ws2, P.PROX_STAGE_UPGATE)
     torch.cuda.synchronize()
     assert int(mc2.item()) == ref[2] and np.array_equal(mi2.cpu().numpy()[0, :ref[2]], ref[1][0, :ref[2]])
+
+
+# ------------------------------------------------------------------ GeGLU layers
+GELU = "gelu_tanh"
+
+
+@pytest.mark.parametrize("name,tokens", [("tiny", [0, 1, 2]), ("qwen3_8b", [0, 1])])
+def test_geglu_decode_parity(P, name, tokens):
+    """A GeGLU layer (GELU-tanh gate) through the same kernels: masks, k_x and
+    y against the oracle with the same activation."""
+    layer, ov = oracle_layer(name)
+    L = pack_layer(layer, activation=P.PROX_ACT_GELU_TANH)
+    tau_x, tau_s = _oracle_taus(ov, n_tok=None if name == "tiny" else 16, act=GELU)
+    _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, f"geglu {name}", act=GELU)
+
+
+def test_geglu_proxy_state_stage2_and_calibration(P):
+    layer, ov = oracle_layer("tiny")
+    L = pack_layer(layer, activation=P.PROX_ACT_GELU_TANH)
+    cfg = layer.cfg
+    # proxy state
+    tau_x = float(np.float32(np.median(np.abs(ov["x_cal"]))))
+    x = to_device(layer.x_dec[[0, 1]], cfg.dtype)
+    st = torch.empty(2, cfg.d_ff, dtype=torch.float32, device="cuda")
+    ws = P.new_workspace(cfg.d_model, cfg.d_ff, 2)
+    P.prox_proxy_state(L, x, tau_x, st, None, ws)
+    torch.cuda.synchronize()
+    for k in range(2):
+        ref = oracle.proxy_state(ov["x_dec"][k], ov["qu"], ov["su"], ov["qg"], ov["sg"], tau_x, act=GELU)
+        assert np.max(np.abs(st.cpu().numpy()[k] - ref["s"])) <= 1e-5 * np.max(np.abs(ref["s"]))
+    # Stage 2 from the oracle's GeGLU channel list
+    tau_x, tau_s = _oracle_taus(ov, act=GELU)
+    ref = oracle.decode(ov["x_dec"][3], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"],
+                        ov["qg"], ov["sg"], tau_x, tau_s, act=GELU)
+    J = np.zeros((1, cfg.d_ff), dtype=np.int32)
+    J[0, : ref["k_s"]] = ref["J"]
+    cnt = np.array([ref["k_s"]], dtype=np.int32)
+    y = torch.empty(1, cfg.d_model, dtype=torch.float32, device="cuda")
+    P.prox_ffn_stage2(L, to_device(layer.x_dec[[3]], cfg.dtype), torch.from_numpy(J).cuda(),
+                      torch.from_numpy(cnt).cuda(), y, ws)
+    torch.cuda.synchronize()
+    assert y_ok(y.cpu().numpy()[0], ref["y"])
+    # calibration: tau_x is activation-free (bit-exact), tau_s uses GELU
+    xc = to_device(layer.x_cal, cfg.dtype)
+    cws = torch.empty(P.prox_calibrate_workspace_size(cfg.d_model, cfg.d_ff, xc.shape[0]),
+                      dtype=torch.uint8, device="cuda")
+    tx, ts = P.prox_calibrate(L, xc, cfg.keep_x, cfg.sparsity_s, cws)
+    assert np.float32(tx) == np.float32(tau_x) and abs(ts - tau_s) <= 1e-5 * tau_s
+    sw_x, sw_s = _oracle_taus(ov)
+    assert abs(sw_s - tau_s) > 1e-3 * tau_s  # the SwiGLU threshold differs

@@ -327,3 +327,42 @@ def test_page_proxy_storage_fraction():
     assert proxy * 6 == ffn_bf16
     # ~12% of all weights when the FFN is ~70% of the model (page's figure)
     assert abs(proxy / ffn_bf16 * 0.70 - _golden()["proxy_storage_overhead"]["value"]) < 0.005
+
+
+# ---------------------------------------------------------------- GeGLU (reading R18)
+def _torch_dense_geglu(x, Wu, Wg, Wd):
+    """GeGLU FFN, y = (x W_up * GELU_tanh(x W_gate)) W_down, via torch."""
+    xt = torch.from_numpy(x)
+    u = xt @ torch.from_numpy(Wu)
+    h = torch.nn.functional.gelu(xt @ torch.from_numpy(Wg), approximate="tanh")
+    return ((u * h) @ torch.from_numpy(Wd)).numpy(), (u * h).numpy()
+
+
+def test_gelu_tanh_matches_library_and_identities():
+    z = np.linspace(-12.0, 12.0, 4801)
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(z), ref, rtol=1e-13, atol=1e-15)
+    # gelu(z) - gelu(-z) = z holds exactly for the tanh form
+    np.testing.assert_allclose(oracle.gelu_tanh(z) - oracle.gelu_tanh(-z), z, rtol=0, atol=1e-13)
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+
+
+def test_geglu_proxy_and_all_pass_decode():
+    layer = _small_layer(48, 96, "bf16", seed=21)
+    Wu, Wg, Wd, X, _ = _f64(layer)
+    ones = np.ones(Wu.shape[0], dtype=np.float32)
+    st = oracle.proxy_state(X[0], Wu, ones, Wg, ones, 0.0, act="gelu_tanh")
+    _, s_ref = _torch_dense_geglu(X[0], Wu, Wg, Wd)
+    np.testing.assert_allclose(st["s"], s_ref, rtol=1e-12, atol=1e-14)
+    qu, su = oracle.pack_proxy(Wu)
+    qg, sg = oracle.pack_proxy(Wg)
+    for t in range(2):
+        out = oracle.decode(X[t], Wu, Wg, Wd, qu, su, qg, sg, 0.0, 0.0, act="gelu_tanh")
+        y_ref, _ = _torch_dense_geglu(X[t], Wu, Wg, Wd)
+        assert np.linalg.norm(out["y"] - y_ref) / np.linalg.norm(y_ref) <= 1e-12
+    # a GeGLU mask differs from the SwiGLU one on the same layer (the
+    # activation really is threaded through)
+    tau = float(np.median(np.abs(X[2])))
+    a = oracle.proxy_state(X[2], qu, su, qg, sg, tau, act="gelu_tanh")["s"]
+    b = oracle.proxy_state(X[2], qu, su, qg, sg, tau)["s"]
+    assert not np.allclose(a, b)
