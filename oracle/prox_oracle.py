@@ -31,6 +31,12 @@ Readings where the pages are silent (each also listed in the design notes):
   R10 SiLU(z) = z / (1 + exp(-z)).
   R13 empty masks give zero output.
   R14 index lists are ascending.
+  R19 the pages' calibration keeps at most 200,000 samples per layer and a
+      4,096-bin histogram; read as: an evenly strided subsample (element
+      floor(i N / M) of the N pooled magnitudes, i < M), linear bins of width
+      w = fp32(max / n_bins) over [0, max], bin = min(n_bins - 1,
+      floor(fp32(v / w))), and the threshold is the lower edge fp32(b * w) of
+      the bin where the count from the top first reaches the keep count.
   R18 GeGLU layers (the pages evaluate GeGLU-style Gemma-3 as well as SwiGLU
       models) use GELU in its tanh form,
       0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), in both the proxy
@@ -231,6 +237,55 @@ def calibrate(X_cal, q_up, sc_up, q_gate, sc_gate, keep_x: float, sparsity_s: fl
     keep_s = 1.0 - float(np.float32(sparsity_s))
     tau_s = order_statistic_keep(s_all, n_keep(keep_s, s_all.size))
     return tau_x32, tau_s
+
+
+def strided_sample(values: np.ndarray, max_samples: int) -> np.ndarray:
+    """At most max_samples of the pooled values: element floor(i N / M) for
+    i < M = min(N, max_samples) (reading R19)."""
+    v = np.asarray(values).ravel()
+    n = v.size
+    m = min(n, int(max_samples))
+    idx = np.array([(i * n) // m for i in range(m)], dtype=np.int64) if m else np.zeros(0, np.int64)
+    return v[idx]
+
+
+def histogram_threshold(samples: np.ndarray, keep_fraction: float, n_bins: int) -> float:
+    """Threshold from a linear n_bins histogram of the sample magnitudes
+    (reading R19): the lower edge of the bin where the count from the top
+    first reaches n_keep(keep_fraction, M).  Bin decisions and the edge are
+    fp32, the precision the stored threshold has."""
+    a = np.abs(np.asarray(samples, dtype=np.float64)).astype(np.float32)
+    keep = n_keep(keep_fraction, a.size)
+    if keep == 0:
+        return math.inf
+    vmax = np.float32(a.max())
+    w = np.float32(vmax / np.float32(n_bins))
+    if w == 0:
+        return 0.0
+    bins = np.minimum(n_bins - 1, np.floor(a / w).astype(np.int64))
+    hist = np.bincount(bins, minlength=n_bins)
+    cum = 0
+    for b in range(n_bins - 1, -1, -1):
+        cum += int(hist[b])
+        if cum >= keep:
+            return float(np.float32(np.float32(b) * w))
+    return 0.0
+
+
+def calibrate_hist(X_cal, q_up, sc_up, q_gate, sc_gate, keep_x: float, sparsity_s: float,
+                   max_samples: int = 200000, n_bins: int = 4096, act="silu"):
+    """Per-layer thresholds the way the pages calibrate ([blog] end-to-end
+    decoding section, calibration paragraph: at most 200,000 samples per layer
+    and a 4,096-bin histogram), with reading R19 for the sampling and binning.
+    tau_s is computed on the proxy state under this tau_x (R6)."""
+    X = np.asarray(X_cal, dtype=np.float64)
+    tau_x = histogram_threshold(strided_sample(np.abs(X), max_samples), float(keep_x), n_bins)
+    s_all = np.concatenate([
+        np.abs(proxy_state(X[t], q_up, sc_up, q_gate, sc_gate, tau_x, act)["s"])
+        for t in range(X.shape[0])])
+    keep_s = 1.0 - float(np.float32(sparsity_s))
+    tau_s = histogram_threshold(strided_sample(s_all, max_samples), keep_s, n_bins)
+    return tau_x, tau_s
 
 
 # --------------------------------------------------------------------------

@@ -366,3 +366,54 @@ def test_geglu_proxy_and_all_pass_decode():
     a = oracle.proxy_state(X[2], qu, su, qg, sg, tau, act="gelu_tanh")["s"]
     b = oracle.proxy_state(X[2], qu, su, qg, sg, tau)["s"]
     assert not np.allclose(a, b)
+
+
+# ---------------------------------------------------------------- histogram calibration (reading R19)
+def test_strided_sample_bruteforce():
+    v = np.arange(10) * 1.5
+    assert list(oracle.strided_sample(v, 4)) == [v[0], v[2], v[5], v[7]]   # floor(i*10/4)
+    assert list(oracle.strided_sample(v, 20)) == list(v)                    # fewer values than M
+    big = np.arange(1000)
+    s = oracle.strided_sample(big, 7)
+    assert list(s) == [(i * 1000) // 7 for i in range(7)]
+
+
+def test_histogram_threshold_brackets_the_order_statistic():
+    """The histogram threshold keeps at least n_keep samples, never more than
+    the next bin's worth, and sits within one bin width below the exact
+    order statistic."""
+    rng = np.random.default_rng(17)
+    for trial in range(30):
+        a = np.abs(rng.laplace(size=5000)).astype(np.float32)
+        keep = float(rng.uniform(0.05, 0.95))
+        nb = int(rng.choice([16, 256, 4096]))
+        t = oracle.histogram_threshold(a, keep, nb)
+        n = oracle.n_keep(keep, a.size)
+        exact = oracle.order_statistic_keep(a, n)
+        w = np.float32(np.float32(a.max()) / np.float32(nb))
+        assert np.sum(a.astype(np.float64) >= t) >= n or t == 0.0
+        assert t <= exact + 1e-12 and exact - t <= float(w) * (1 + 1e-6)
+    # edges
+    a = np.abs(rng.normal(size=100)).astype(np.float32)
+    assert math.isinf(oracle.histogram_threshold(a, 0.0, 64))
+    assert oracle.histogram_threshold(a, 1.0, 64) == 0.0
+    assert oracle.histogram_threshold(np.zeros(10, np.float32), 0.5, 64) == 0.0
+
+
+def test_calibrate_hist_close_to_exact_calibration():
+    layer = _small_layer(64, 128, "f32", seed=23)
+    Wu, Wg, Wd, X, Xc = _f64(layer)
+    qu, su = oracle.pack_proxy(Wu)
+    qg, sg = oracle.pack_proxy(Wg)
+    tx_e, ts_e = oracle.calibrate(Xc, qu, su, qg, sg, 0.5, 0.7)
+    tx_h, ts_h = oracle.calibrate_hist(Xc, qu, su, qg, sg, 0.5, 0.7, max_samples=200000, n_bins=4096)
+    # every sample is kept (N < 200k), so tau_x is within one bin below the exact one
+    wx = float(np.float32(np.float32(np.abs(Xc).max()) / np.float32(4096)))
+    assert tx_h <= tx_e and tx_e - tx_h <= wx * (1 + 1e-6)
+    # tau_s: within one bin below the exact statistic of the same pool (the
+    # proxy state under tau_x from the histogram)
+    pool = np.concatenate([np.abs(oracle.proxy_state(Xc[t], qu, su, qg, sg, tx_h)["s"])
+                           for t in range(Xc.shape[0])])
+    exact_s = oracle.order_statistic_keep(pool.astype(np.float32), oracle.n_keep(1.0 - float(np.float32(0.7)), pool.size))
+    ws_ = float(np.float32(np.float32(pool.astype(np.float32).max()) / np.float32(4096)))
+    assert ts_h <= exact_s and exact_s - ts_h <= ws_ * (1 + 1e-6)
