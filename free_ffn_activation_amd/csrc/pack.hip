@@ -115,7 +115,69 @@ __global__ __launch_bounds__(kThreads) void digit_hist_kernel(const void* v, siz
   if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], h[threadIdx.x]);
 }
 
+// |v[floor(i N / M)]| for i < M as fp32 (an evenly strided sample), and the
+// sample maximum: fp32 bits of non-negative values order as unsigned ints, so
+// one atomicMax per block on the bits gives the maximum.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sample_abs_kernel(const void* v, uint64_t n, uint32_t m, float* out,
+                                                               uint32_t* maxbits) {
+  __shared__ uint32_t s_max[kThreads / 64];
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  float a = 0.f;
+  if (i < m) {
+    a = fabsf(load_elem<T>(v, (static_cast<uint64_t>(i) * n) / m));
+    out[i] = a;
+  }
+  uint32_t bits = __float_as_uint(a);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) bits = max(bits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), o, 64)));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = bits;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = s_max[0];
+    for (int k = 1; k < kThreads / 64; ++k) b = max(b, s_max[k]);
+    atomicMax(maxbits, b);
+  }
+}
+
+// Linear histogram: bin = min(nb - 1, floor(v / w)) with an IEEE fp32
+// division, counted in LDS and added to the global counts.
+__global__ __launch_bounds__(kThreads) void bin_hist_kernel(const float* v, uint32_t m, float w, int nb,
+                                                             uint32_t* hist) {
+  extern __shared__ uint32_t h[];
+  for (int b = threadIdx.x; b < nb; b += kThreads) h[b] = 0u;
+  __syncthreads();
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < m; i += stride) {
+    const float q = __fdiv_rn(v[i], w);
+    const int b = q >= static_cast<float>(nb) ? nb - 1 : static_cast<int>(q);
+    atomicAdd(&h[b], 1u);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += kThreads)
+    if (h[b]) atomicAdd(&hist[b], h[b]);
+}
+
 }  // namespace
+
+hipError_t launch_sample_abs(const void* v, uint64_t n, int vdtype, uint32_t m, float* out, uint32_t* maxbits,
+                             hipStream_t s) {
+  const unsigned blocks = (m + kThreads - 1) / kThreads;
+  if (vdtype == PROX_BF16)
+    hipLaunchKernelGGL((sample_abs_kernel<Bf16Tag>), dim3(blocks), dim3(kThreads), 0, s, v, n, m, out, maxbits);
+  else
+    hipLaunchKernelGGL((sample_abs_kernel<F32Tag>), dim3(blocks), dim3(kThreads), 0, s, v, n, m, out, maxbits);
+  return hipGetLastError();
+}
+
+hipError_t launch_bin_hist(const float* v, uint32_t m, float w, int nb, uint32_t* hist, hipStream_t s) {
+  unsigned blocks = (m + kThreads - 1) / kThreads;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(bin_hist_kernel, dim3(blocks), dim3(kThreads), static_cast<size_t>(nb) * 4, s, v, m, w, nb,
+                     hist);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int qstride, int wdtype,
                        uint8_t* proxy_q, float* proxy_scale, void* w_upgate_t, hipStream_t s) {

@@ -260,6 +260,81 @@ size_t calib_bytes(const Plan& p, int32_t n_tokens) {
          p.tok_bytes * std::min<int32_t>(n_tokens, kCalChunk) + 1024;
 }
 
+constexpr uint32_t kMaxHistSamples = 1u << 24;  // keeps i * N below 2^64
+constexpr int kMaxHistBins = 8192;              // the LDS histogram of one block
+
+size_t calib_hist_bytes(const Plan& p, int32_t n_tokens, uint32_t max_samples, int n_bins) {
+  return calib_bytes(p, n_tokens) + align256(static_cast<size_t>(max_samples) * sizeof(float)) +
+         align256(static_cast<size_t>(n_bins) * sizeof(uint32_t)) + 256;
+}
+
+// Threshold from an evenly strided sample of at most max_samples of the n
+// values |v| and a linear nb-bin histogram over [0, max]: the lower edge of
+// the bin where the count from the top first reaches ceil(keep * m).  Bin
+// decisions use IEEE fp32 divisions; the edge is fp32(b * w).  Blocks.
+prox_status hist_threshold(const void* v, uint64_t n, int vdtype, double keep, uint32_t max_samples, int nb,
+                           float* samples, uint32_t* hist_dev, uint32_t* max_dev, hipStream_t s, float* out) {
+  const uint32_t m = static_cast<uint32_t>(std::min<uint64_t>(n, max_samples));
+  const uint64_t keep_n = keep_count(keep, m);
+  if (keep_n == 0) {
+    *out = INFINITY;
+    return PROX_OK;
+  }
+  hipError_t e = launch_fill_zero(max_dev, sizeof(uint32_t), s);
+  if (e != hipSuccess) return hip_fail(e, "sample maximum clear");
+  e = launch_sample_abs(v, n, vdtype, m, samples, max_dev, s);
+  if (e != hipSuccess) return hip_fail(e, "sample launch");
+  uint32_t maxbits = 0;
+  e = hipMemcpyAsync(&maxbits, max_dev, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "sample maximum copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "calibration synchronisation");
+  float vmax;
+  std::memcpy(&vmax, &maxbits, 4);
+  if (!std::isfinite(vmax)) return fail(PROX_ERR_INVALID_ARG, "calibration values are not all finite");
+  const float w = vmax / static_cast<float>(nb);
+  if (!(w > 0.f)) {
+    *out = 0.f;
+    return PROX_OK;
+  }
+  e = launch_fill_zero(hist_dev, static_cast<size_t>(nb) * sizeof(uint32_t), s);
+  if (e != hipSuccess) return hip_fail(e, "histogram clear");
+  e = launch_bin_hist(samples, m, w, nb, hist_dev, s);
+  if (e != hipSuccess) return hip_fail(e, "histogram launch");
+  std::vector<uint32_t> hist(static_cast<size_t>(nb));
+  e = hipMemcpyAsync(hist.data(), hist_dev, static_cast<size_t>(nb) * sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "histogram copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "calibration synchronisation");
+  uint64_t cum = 0;
+  for (int b = nb - 1; b >= 0; --b) {
+    cum += hist[b];
+    if (cum >= keep_n) {
+      *out = static_cast<float>(b) * w;
+      return PROX_OK;
+    }
+  }
+  *out = 0.f;
+  return PROX_OK;
+}
+
+// s~ of every calibration token under tau_x into s_all ([n_tokens][f] fp32),
+// in chunks of kCalChunk tokens on the workspace slice tws.
+prox_status proxy_state_all(const Plan& p, const prox_layer* layer, const void* X_cal, int32_t n_tokens,
+                            float tau_x, float* s_all, uint8_t* tws, hipStream_t s) {
+  const int chunk = std::min<int32_t>(n_tokens, kCalChunk);
+  const size_t es = elem_size(layer->wdtype);
+  for (int t0 = 0; t0 < n_tokens; t0 += chunk) {
+    const int nb = std::min(chunk, n_tokens - t0);
+    const void* xt = static_cast<const uint8_t*>(X_cal) + static_cast<size_t>(t0) * p.d * es;
+    const hipError_t e = launch_stage1(stage1_args(p, layer, xt, tau_x, INFINITY, tws,
+                                                   s_all + static_cast<size_t>(t0) * p.f, nullptr),
+                                       layer->wdtype, nb, true, s);
+    if (e != hipSuccess) return hip_fail(e, "stage-1 launch (calibration)");
+  }
+  return PROX_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -406,6 +481,78 @@ PROX_API prox_status prox_budget_s2(float e_target, float s1, float alpha, float
                 static_cast<double>(e_target), static_cast<double>(s1), static_cast<double>(alpha), s2);
   *s2_out = static_cast<float>(s2);
   return PROX_OK;
+}
+
+PROX_API prox_status prox_calibrate_hist_workspace_size(int32_t d, int32_t f, int32_t n_tokens,
+                                                        int32_t max_samples, int32_t n_bins, size_t* bytes) {
+  try {
+    g_err.clear();
+    if (!bytes) return fail(PROX_ERR_INVALID_ARG, "bytes is NULL");
+    prox_status st = check_shape(d, f, PROX_BF16);
+    if (st != PROX_OK) return st;
+    if (n_tokens < 1 || n_tokens > 65536)
+      return fail(PROX_ERR_INVALID_ARG, "n_tokens %d outside [1, 65536]", n_tokens);
+    if (max_samples < 1 || static_cast<uint32_t>(max_samples) > kMaxHistSamples || n_bins < 2 ||
+        n_bins > kMaxHistBins)
+      return fail(PROX_ERR_INVALID_ARG, "max_samples %d outside [1, %u] or n_bins %d outside [2, %d]", max_samples,
+                  kMaxHistSamples, n_bins, kMaxHistBins);
+    *bytes = calib_hist_bytes(make_plan(d, f, PROX_BF16), n_tokens, static_cast<uint32_t>(max_samples), n_bins);
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_calibrate_hist(const prox_layer* layer, const void* X_cal, int32_t n_tokens,
+                                         float keep_x, float sparsity_s, int32_t max_samples, int32_t n_bins,
+                                         float* tau_x, float* tau_s, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    prox_status st = check_layer(layer);
+    if (st != PROX_OK) return st;
+    if (!X_cal || !tau_x || !tau_s) return fail(PROX_ERR_INVALID_ARG, "X_cal, tau_x, tau_s must be non-NULL");
+    if (!aligned(X_cal, 16)) return fail(PROX_ERR_INVALID_ARG, "X_cal must be 16-byte aligned");
+    if (n_tokens < 1 || n_tokens > 65536)
+      return fail(PROX_ERR_INVALID_ARG, "n_tokens %d outside [1, 65536]", n_tokens);
+    if (!(keep_x >= 0.f && keep_x <= 1.f) || !(sparsity_s >= 0.f && sparsity_s <= 1.f))
+      return fail(PROX_ERR_INVALID_ARG, "keep_x and sparsity_s must lie in [0, 1]");
+    if (max_samples < 1 || static_cast<uint32_t>(max_samples) > kMaxHistSamples || n_bins < 2 ||
+        n_bins > kMaxHistBins)
+      return fail(PROX_ERR_INVALID_ARG, "max_samples %d outside [1, %u] or n_bins %d outside [2, %d]", max_samples,
+                  kMaxHistSamples, n_bins, kMaxHistBins);
+    const Plan p = make_plan(layer->d_model, layer->d_ff, layer->wdtype);
+    if (!ws || !aligned(ws, 256)) return fail(PROX_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+    const size_t need = calib_hist_bytes(p, n_tokens, static_cast<uint32_t>(max_samples), n_bins);
+    if (ws_bytes < need)
+      return fail(PROX_ERR_INVALID_ARG, "calibration workspace of %zu bytes is smaller than the %zu needed",
+                  ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    float* s_all = reinterpret_cast<float*>(base);
+    uint8_t* tws = base + align256(static_cast<size_t>(n_tokens) * p.f * sizeof(float));
+    const int chunk = std::min<int32_t>(n_tokens, kCalChunk);
+    float* samples = reinterpret_cast<float*>(base + calib_bytes(p, n_tokens));
+    uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(samples) +
+                                                 align256(static_cast<size_t>(max_samples) * sizeof(float)));
+    uint32_t* maxw = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(hist) +
+                                                 align256(static_cast<size_t>(n_bins) * sizeof(uint32_t)));
+    hipError_t e = launch_fill_zero(tws, p.tok_bytes * chunk, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace fill");
+    float tx = 0.f;
+    st = hist_threshold(X_cal, static_cast<uint64_t>(n_tokens) * p.d, layer->wdtype, static_cast<double>(keep_x),
+                        static_cast<uint32_t>(max_samples), n_bins, samples, hist, maxw, s, &tx);
+    if (st != PROX_OK) return st;
+    if ((st = proxy_state_all(p, layer, X_cal, n_tokens, tx, s_all, tws, s)) != PROX_OK) return st;
+    float ts = 0.f;
+    st = hist_threshold(s_all, static_cast<uint64_t>(n_tokens) * p.f, PROX_F32, 1.0 - static_cast<double>(sparsity_s),
+                        static_cast<uint32_t>(max_samples), n_bins, samples, hist, maxw, s, &ts);
+    if (st != PROX_OK) return st;
+    *tau_x = tx;
+    *tau_s = ts;
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
 }
 
 PROX_API prox_status prox_workspace_init(void* ws, size_t ws_bytes, void* stream) {

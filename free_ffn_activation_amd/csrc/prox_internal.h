@@ -90,6 +90,12 @@ int proxy_row_stride(int f);
 hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int qstride, int wdtype,
                        uint8_t* proxy_q, float* proxy_scale, void* w_upgate_t, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Histogram calibration: |v| at n evenly strided positions (m of n values)
+// into out, with the maximum's fp32 bits atomically maxed into *maxbits; and
+// a linear nb-bin histogram of m non-negative values with bin width w.
+hipError_t launch_sample_abs(const void* v, uint64_t n, int vdtype, uint32_t m, float* out, uint32_t* maxbits,
+                             hipStream_t s);
+hipError_t launch_bin_hist(const float* v, uint32_t m, float w, int nb, uint32_t* hist, hipStream_t s);
 // Calibration helpers: histogram of 8-bit digits of |v| keys that match a
 // prefix; keys are fp32 bit patterns of |value| (values in wdtype or fp32).
 hipError_t launch_digit_histogram(const void* v, size_t n, int vdtype, uint32_t prefix,

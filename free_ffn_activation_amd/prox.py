@@ -35,7 +35,7 @@ _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPO
 EXPORTED = ("prox_abi_version", "prox_last_error", "prox_layer_sizes", "prox_workspace_size",
             "prox_calibrate_workspace_size", "prox_budget_effective", "prox_budget_s2",
             "prox_workspace_init", "prox_pack_proxy",
-            "prox_calibrate", "prox_ffn_decode", "prox_ffn_decode_events",
+            "prox_calibrate", "prox_calibrate_hist_workspace_size", "prox_calibrate_hist", "prox_ffn_decode", "prox_ffn_decode_events",
             "prox_ffn_decode_stages", "prox_ffn_stage2", "prox_proxy_state")
 
 
@@ -66,6 +66,9 @@ _sig = {
     "prox_layer_sizes": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
     "prox_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
     "prox_budget_effective": (_c_i32, [_c_f32, _c_f32, _c_f32, _P(_c_f32)]),
+    "prox_calibrate_hist_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _P(_c_size)]),
+    "prox_calibrate_hist": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_i32, _c_i32,
+                                     _P(_c_f32), _P(_c_f32), _c_vp, _c_size, _c_vp]),
     "prox_budget_s2": (_c_i32, [_c_f32, _c_f32, _c_f32, _P(_c_f32)]),
     "prox_calibrate_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
     "prox_workspace_init": (_c_i32, [_c_vp, _c_size, _c_vp]),
@@ -227,6 +230,26 @@ def prox_calibrate(layer: ProxLayer, X_cal: torch.Tensor, keep_x: float, sparsit
     _check(_lib.prox_calibrate(ctypes.byref(layer.desc), _ptr(X_cal), X_cal.shape[0], keep_x,
                                sparsity_s, ctypes.byref(tx), ctypes.byref(ts), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
+    return float(tx.value), float(ts.value)
+
+
+def prox_calibrate_hist_workspace_size(d_model: int, d_ff: int, n_tokens: int, max_samples: int = 200000,
+                                       n_bins: int = 4096) -> int:
+    out = _c_size(0)
+    _check(_lib.prox_calibrate_hist_workspace_size(d_model, d_ff, n_tokens, max_samples, n_bins,
+                                                   ctypes.byref(out)))
+    return int(out.value)
+
+
+def prox_calibrate_hist(layer: ProxLayer, X_cal: torch.Tensor, keep_x: float, sparsity_s: float,
+                        ws: torch.Tensor, max_samples: int = 200000, n_bins: int = 4096, stream=None):
+    """Histogram calibration (blocking).  Returns (tau_x, tau_s)."""
+    if X_cal.dim() != 2 or X_cal.shape[1] != layer.d_model or _wdtype_of(X_cal) != layer.wdtype:
+        raise ValueError("X_cal must be [n_tokens, d_model] in the layer dtype")
+    tx, ts = _c_f32(0.0), _c_f32(0.0)
+    _check(_lib.prox_calibrate_hist(ctypes.byref(layer.desc), _ptr(X_cal), X_cal.shape[0], keep_x, sparsity_s,
+                                    max_samples, n_bins, ctypes.byref(tx), ctypes.byref(ts), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
     return float(tx.value), float(ts.value)
 
 

@@ -181,6 +181,29 @@ prox_status prox_calibrate(const prox_layer* layer, const void* X_cal, int32_t n
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Calibration the way the pages describe it ([blog] end-to-end decoding
+ * section, calibration paragraph: at most 200,000 activation samples per
+ * layer and a 4,096-bin histogram).  The pages leave the sampling and the
+ * binning open; this call takes, for each threshold, the values at positions
+ * floor(i N / M), i < M = min(N, max_samples), of the N pooled magnitudes
+ * (|X_cal| for tau_x; |s~| under this tau_x for tau_s), bins them linearly
+ * with width w = fp32(max / n_bins) (bin = min(n_bins - 1, floor(fp32(v /
+ * w)))), and returns the lower edge fp32(b * w) of the bin where the count
+ * from the top first reaches ceil(keep * M) (keep = keep_x, or 1 - sparsity_s
+ * in double); keep 0 gives +inf, an all-zero sample 0.  The threshold keeps
+ * at least the requested fraction of the sample (the whole bin is kept).
+ *   max_samples in [1, 2^24], n_bins in [2, 8192] (the pages: 200000, 4096)
+ *   ws          device, >= prox_calibrate_hist_workspace_size bytes
+ * Non-finite calibration values give PROX_ERR_INVALID_ARG.  Other arguments
+ * as prox_calibrate; BLOCKS until done.
+ */
+prox_status prox_calibrate_hist_workspace_size(int32_t d_model, int32_t d_ff, int32_t n_tokens,
+                                               int32_t max_samples, int32_t n_bins, size_t* bytes);
+prox_status prox_calibrate_hist(const prox_layer* layer, const void* X_cal, int32_t n_tokens,
+                                float keep_x, float sparsity_s, int32_t max_samples, int32_t n_bins,
+                                float* tau_x, float* tau_s, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * One decode step through one FFN layer for `batch` independent tokens
  * (each token gets its own masks).
  *   x           device [batch][d_model] in wdtype

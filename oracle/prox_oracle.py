@@ -279,7 +279,8 @@ def calibrate_hist(X_cal, q_up, sc_up, q_gate, sc_gate, keep_x: float, sparsity_
     and a 4,096-bin histogram), with reading R19 for the sampling and binning.
     tau_s is computed on the proxy state under this tau_x (R6)."""
     X = np.asarray(X_cal, dtype=np.float64)
-    tau_x = histogram_threshold(strided_sample(np.abs(X), max_samples), float(keep_x), n_bins)
+    # keep fractions arrive as fp32 values (the ABI's type), widened exactly
+    tau_x = histogram_threshold(strided_sample(np.abs(X), max_samples), float(np.float32(keep_x)), n_bins)
     s_all = np.concatenate([
         np.abs(proxy_state(X[t], q_up, sc_up, q_gate, sc_gate, tau_x, act)["s"])
         for t in range(X.shape[0])])

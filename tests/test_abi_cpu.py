@@ -121,6 +121,18 @@ def test_other_entry_points_validate():
     assert lib.prox_ffn_decode_events(ctypes.byref(L), FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE, None,
                                       FAKE, 1 << 30, None, None) == P.PROX_ERR_INVALID_ARG
     assert lib.prox_workspace_init(None, 16, None) == P.PROX_ERR_INVALID_ARG
+    # histogram calibration: bins / samples out of range, small workspace, bad fraction
+    size = ctypes.c_size_t(0)
+    assert lib.prox_calibrate_hist_workspace_size(256, 768, 64, 200000, 4096, ctypes.byref(size)) == P.PROX_OK
+    assert size.value >= 64 * 768 * 4 + 200000 * 4 + 4096 * 4
+    for ms, nb in ((0, 4096), (200000, 1), (200000, 8193), (1 << 25, 4096)):
+        assert lib.prox_calibrate_hist_workspace_size(256, 768, 64, ms, nb, ctypes.byref(size)) == P.PROX_ERR_INVALID_ARG
+        assert lib.prox_calibrate_hist(ctypes.byref(L), FAKE, 64, 0.5, 0.7, ms, nb, ctypes.byref(tx),
+                                       ctypes.byref(ts), FAKE, 1 << 30, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_calibrate_hist(ctypes.byref(L), FAKE, 64, 0.5, 0.7, 200000, 4096, ctypes.byref(tx),
+                                   ctypes.byref(ts), FAKE, 16, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_calibrate_hist(ctypes.byref(L), FAKE, 64, 0.5, 1.5, 200000, 4096, ctypes.byref(tx),
+                                   ctypes.byref(ts), FAKE, 1 << 30, None) == P.PROX_ERR_INVALID_ARG
     # stage subsets must be a non-empty subset of the three kernels
     for bad in (0, 8, -1):
         assert lib.prox_ffn_decode_stages(ctypes.byref(L), FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE,

@@ -453,3 +453,78 @@ def test_geglu_proxy_state_stage2_and_calibration(P):
     assert np.float32(tx) == np.float32(tau_x) and abs(ts - tau_s) <= 1e-5 * tau_s
     sw_x, sw_s = _oracle_taus(ov)
     assert abs(sw_s - tau_s) > 1e-3 * tau_s  # the SwiGLU threshold differs
+
+
+# ------------------------------------------------------------------ histogram calibration
+def _bin_width(values, n_bins):
+    a = np.abs(np.asarray(values, dtype=np.float64)).astype(np.float32)
+    return float(np.float32(np.float32(a.max()) / np.float32(n_bins)))
+
+
+@pytest.mark.parametrize("name,n_tok,max_samples", [("tiny", 64, 200000), ("qwen3_8b", 16, 50000)])
+def test_calibrate_hist_parity(P, name, n_tok, max_samples):
+    """tau_x bit-exact (the same strided samples of exact values, fp32 bin
+    decisions); tau_s within one bin of the oracle's (its samples are fp32
+    GPU proxy states against the oracle's fp64 ones)."""
+    layer, ov = oracle_layer(name)
+    L = pack_layer(layer)
+    cfg = layer.cfg
+    nb = 4096
+    xc = to_device(layer.x_cal[:n_tok], cfg.dtype)
+    ws = torch.empty(P.prox_calibrate_hist_workspace_size(cfg.d_model, cfg.d_ff, n_tok, max_samples, nb),
+                     dtype=torch.uint8, device="cuda")
+    tx, ts = P.prox_calibrate_hist(L, xc, cfg.keep_x, cfg.sparsity_s, ws, max_samples, nb)
+    Xc = ov["x_cal"][:n_tok]
+    rx, rs = oracle.calibrate_hist(Xc, ov["qu"], ov["su"], ov["qg"], ov["sg"], cfg.keep_x, cfg.sparsity_s,
+                                   max_samples=max_samples, n_bins=nb)
+    pool = np.concatenate([oracle.proxy_state(Xc[t], ov["qu"], ov["su"], ov["qg"], ov["sg"], rx)["s"]
+                           for t in range(n_tok)])
+    ws_bin = _bin_width(oracle.strided_sample(np.abs(pool), max_samples), nb)
+    print(f"[calibrate_hist {name}] tau_x gpu={tx!r} oracle={rx!r}  tau_s gpu={ts!r} oracle={rs!r} bin={ws_bin:.3e}")
+    assert np.float32(tx) == np.float32(rx)
+    assert abs(ts - rs) <= 1.01 * ws_bin
+    # edges: keep everything -> 0, keep nothing -> +inf
+    tx0, ts0 = P.prox_calibrate_hist(L, xc, 1.0, 0.0, ws, max_samples, nb)
+    assert tx0 == 0.0 and ts0 == 0.0
+    tx1, ts1 = P.prox_calibrate_hist(L, xc, 0.0, 1.0, ws, max_samples, nb)
+    assert math.isinf(tx1) and math.isinf(ts1)
+
+
+def test_depth_ordered_calibration_on_a_chain(P):
+    """The pages calibrate layer by layer in depth order, each on the previous
+    layers' sparse outputs.  A chain of three tiny fp32 layers, x_{l+1} =
+    x_l + y_l: per-layer thresholds within one histogram bin of the oracle's
+    chain, the first layer's tau_x bit-exact."""
+    nb, ms = 4096, 200000
+    cfg = synth.CONFIGS["tiny"]
+    layers = [synth.make_layer(cfg, l, n_dec=2) for l in range(3)]
+    X = synth.as_f64(layers[0].x_cal, "f32")            # the chain's input
+    Xg = to_device(layers[0].x_cal, "f32")
+    n = X.shape[0]
+    ws_cal = torch.empty(P.prox_calibrate_hist_workspace_size(cfg.d_model, cfg.d_ff, n, ms, nb),
+                         dtype=torch.uint8, device="cuda")
+    ws = P.new_workspace(cfg.d_model, cfg.d_ff, n)
+    y = torch.empty(n, cfg.d_model, dtype=torch.float32, device="cuda")
+    mi = torch.empty(n, cfg.d_ff, dtype=torch.int32, device="cuda")
+    mc = torch.empty(n, dtype=torch.int32, device="cuda")
+    for l, lay in enumerate(layers):
+        ov = oracle_view(lay)
+        L = pack_layer(lay)
+        tx, ts = P.prox_calibrate_hist(L, Xg, cfg.keep_x, cfg.sparsity_s, ws_cal, ms, nb)
+        rx, rs = oracle.calibrate_hist(X, ov["qu"], ov["su"], ov["qg"], ov["sg"], cfg.keep_x, cfg.sparsity_s,
+                                       max_samples=ms, n_bins=nb)
+        wx = _bin_width(X, nb)
+        pool = np.concatenate([oracle.proxy_state(X[t], ov["qu"], ov["su"], ov["qg"], ov["sg"], rx)["s"]
+                               for t in range(n)])
+        wsb = _bin_width(pool, nb)
+        print(f"[chain layer {l}] tau_x {tx!r}/{rx!r} tau_s {ts!r}/{rs!r}")
+        if l == 0:
+            assert np.float32(tx) == np.float32(rx)
+        assert abs(tx - rx) <= 1.01 * wx and abs(ts - rs) <= 1.01 * wsb
+        # this layer's sparse outputs feed the next layer's calibration
+        P.prox_ffn_decode(L, Xg, tx, ts, y, mi, mc, None, ws)
+        torch.cuda.synchronize()
+        Xg = (Xg + y).contiguous()
+        Y = np.stack([oracle.decode(X[t], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"], ov["qg"], ov["sg"],
+                                    rx, rs)["y"] for t in range(n)])
+        X = (X + Y).astype(np.float32).astype(np.float64)
