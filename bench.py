@@ -453,6 +453,80 @@ def main() -> int:
                   "t_dense_projection_own_us": round(t_proj_own, 3), "operating_points": op_out}
         del bws, wug2, xb2
 
+    # ---------------------------------------------------------------- depth-ordered calibration
+    # The pages calibrate with at most 200,000 samples and a 4,096-bin
+    # histogram per layer, in depth order, and report the runtime effective
+    # sparsity against each target.  Here the rotation's layers form a chain
+    # with a residual stream h (fp32): h_0 = x_0, h_{l+1} = h_l + y_l, and layer
+    # l+1 reads x_{l+1} = bf16(RMSNorm(h_{l+1})) (unit RMS per token, as a
+    # transformer normalises the FFN input); for each target e at s1 = 0.7 (s2 from the
+    # budget allocator with the measured alpha) every layer is calibrated on
+    # the chain's calibration tokens after the earlier layers ran sparse, then
+    # held-out tokens run through the chain and their keep fractions give the
+    # runtime effective sparsity.
+    calibration = None
+    if not args.no_budget:
+        nb_h, ms_h = 4096, 200000
+        n_cal = x_cal[0].shape[0]
+        hws = torch.empty(prox.prox_calibrate_hist_workspace_size(d, f, n_cal, ms_h, nb_h), dtype=torch.uint8,
+                          device=dev)
+        cws = prox.new_workspace(d, f, n_cal)
+        cy = torch.empty(n_cal, d, dtype=torch.float32, device=dev)
+        cmi = torch.empty(n_cal, f, dtype=torch.int32, device=dev)
+        cmc = torch.empty(n_cal, dtype=torch.int32, device=dev)
+        hy = torch.empty(n_tok, d, dtype=torch.float32, device=dev)
+        hmi = torch.empty(n_tok, f, dtype=torch.int32, device=dev)
+        hmc = torch.empty(n_tok, dtype=torch.int32, device=dev)
+        hic = torch.empty(n_tok, dtype=torch.int32, device=dev)
+        hdws = prox.new_workspace(d, f, n_tok)
+
+        def rms_norm_bf16(h):  # fp32 residual stream -> bf16 bits of the normalised FFN input
+            xn = h * torch.rsqrt(torch.mean(h * h, dim=-1, keepdim=True) + 1e-6)
+            return xn.to(torch.bfloat16).view(torch.int16).contiguous()
+
+        targets = []
+        t_cal0 = time.perf_counter()
+        for e_t in (0.4, 0.5, 0.6, 0.7):
+            s1c = 0.7
+            s2c = prox.prox_budget_s2(e_t, s1c, alpha)
+            xc_chain = x_cal[0].clone()
+            hc = xc_chain.view(torch.bfloat16).float()
+            thr = []
+            for l in range(n_layers):
+                tx, ts = prox.prox_calibrate_hist(layers[l], xc_chain, 1.0 - s1c, s2c, hws, ms_h, nb_h)
+                thr.append((tx, ts))
+                prox.prox_ffn_decode(layers[l], xc_chain, tx, ts, cy, cmi, cmc, None, cws)
+                hc = hc + cy
+                xc_chain = rms_norm_bf16(hc)
+            xh = x_all[0].clone()
+            hh = xh.view(torch.bfloat16).float()
+            kx_l, ks_l, e_l = [], [], []
+            for l in range(n_layers):
+                prox.prox_ffn_decode(layers[l], xh, thr[l][0], thr[l][1], hy, hmi, hmc, hic, hdws)
+                torch.cuda.synchronize()
+                kx_f = float(hic.float().mean()) / d
+                ks_f = float(hmc.float().mean()) / f
+                kx_l.append(kx_f)
+                ks_l.append(ks_f)
+                e_l.append(prox.prox_budget_effective(1.0 - kx_f, 1.0 - ks_f, alpha))
+                hh = hh + hy
+                xh = rms_norm_bf16(hh)
+            e_run = float(np.mean(e_l))
+            targets.append({"e_target": e_t, "s1": s1c, "s2": round(s2c, 4),
+                            "runtime_keep_x_mean": round(float(np.mean(kx_l)), 4),
+                            "runtime_keep_s_mean": round(float(np.mean(ks_l)), 4),
+                            "runtime_effective_mean": round(e_run, 4),
+                            "shortfall_points": round(100.0 * (e_t - e_run), 2),
+                            "per_layer_effective": [round(v, 4) for v in e_l]})
+            log(f"depth-ordered calibration, target e={e_t}: runtime effective {e_run:.4f} "
+                f"({100.0 * (e_t - e_run):+.2f} points short)")
+        calibration = {"method": f"histogram, at most {ms_h} samples, {nb_h} bins, depth order on a chain of "
+                                 f"the {n_layers} layers (h_(l+1) = h_l + y_l, x_(l+1) = bf16(RMSNorm(h_(l+1)))), {n_cal} calibration tokens, "
+                                 f"{n_tok} held-out tokens",
+                       "alpha": round(alpha, 4), "targets": targets,
+                       "seconds": round(time.perf_counter() - t_cal0, 2)}
+        del hws, cws, hdws
+
     # ---------------------------------------------------------------- GeGLU layers
     # the same packed layers read as GeGLU (GELU-tanh gate), recalibrated at the
     # headline keep / sparsity, timed over the same rotation
@@ -548,6 +622,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "budget": budget,
         "geglu": geglu,
+        "calibration": calibration,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -492,14 +492,16 @@ def test_calibrate_hist_parity(P, name, n_tok, max_samples):
 
 def test_depth_ordered_calibration_on_a_chain(P):
     """The pages calibrate layer by layer in depth order, each on the previous
-    layers' sparse outputs.  A chain of three tiny fp32 layers, x_{l+1} =
-    x_l + y_l: per-layer thresholds within one histogram bin of the oracle's
-    chain, the first layer's tau_x bit-exact."""
+    layers' sparse outputs.  A chain of three tiny fp32 layers with a residual
+    stream, h_{l+1} = h_l + y_l, x_{l+1} = RMSNorm(h_{l+1}): per-layer
+    thresholds within one histogram bin of the oracle's chain, the first
+    layer's tau_x bit-exact."""
     nb, ms = 4096, 200000
     cfg = synth.CONFIGS["tiny"]
     layers = [synth.make_layer(cfg, l, n_dec=2) for l in range(3)]
     X = synth.as_f64(layers[0].x_cal, "f32")            # the chain's input
     Xg = to_device(layers[0].x_cal, "f32")
+    H, Hg = X.copy(), Xg.clone()
     n = X.shape[0]
     ws_cal = torch.empty(P.prox_calibrate_hist_workspace_size(cfg.d_model, cfg.d_ff, n, ms, nb),
                          dtype=torch.uint8, device="cuda")
@@ -524,7 +526,9 @@ def test_depth_ordered_calibration_on_a_chain(P):
         # this layer's sparse outputs feed the next layer's calibration
         P.prox_ffn_decode(L, Xg, tx, ts, y, mi, mc, None, ws)
         torch.cuda.synchronize()
-        Xg = (Xg + y).contiguous()
+        Hg = Hg + y
+        Xg = (Hg * torch.rsqrt(torch.mean(Hg * Hg, dim=-1, keepdim=True) + 1e-6)).contiguous()
         Y = np.stack([oracle.decode(X[t], ov["Wu"], ov["Wg"], ov["Wd"], ov["qu"], ov["su"], ov["qg"], ov["sg"],
                                     rx, rs)["y"] for t in range(n)])
-        X = (X + Y).astype(np.float32).astype(np.float64)
+        H = H + Y
+        X = (H / np.sqrt(np.mean(H * H, axis=-1, keepdims=True) + 1e-6)).astype(np.float32).astype(np.float64)
