@@ -420,6 +420,8 @@ def main() -> int:
             try:
                 s2 = prox.prox_budget_s2(e_t, s1, a)
             except prox.ProxError as exc:
+                if exc.status != prox.PROX_ERR_UNSUPPORTED:
+                    raise
                 op_out.append({"alpha_from": label, "e_target": e_t, "s1": s1, "alpha": round(a, 4),
                                "reachable": False, "reason": str(exc)})
                 continue
@@ -488,7 +490,13 @@ def main() -> int:
         t_cal0 = time.perf_counter()
         for e_t in (0.4, 0.5, 0.6, 0.7):
             s1c = 0.7
-            s2c = prox.prox_budget_s2(e_t, s1c, alpha)
+            try:
+                s2c = prox.prox_budget_s2(e_t, s1c, alpha)
+            except prox.ProxError as exc:  # target out of reach at this alpha
+                if exc.status != prox.PROX_ERR_UNSUPPORTED:
+                    raise
+                targets.append({"e_target": e_t, "s1": s1c, "reachable": False, "reason": str(exc)})
+                continue
             xc_chain = x_cal[0].clone()
             hc = xc_chain.view(torch.bfloat16).float()
             thr = []
@@ -512,7 +520,7 @@ def main() -> int:
                 hh = hh + hy
                 xh = rms_norm_bf16(hh)
             e_run = float(np.mean(e_l))
-            targets.append({"e_target": e_t, "s1": s1c, "s2": round(s2c, 4),
+            targets.append({"e_target": e_t, "s1": s1c, "s2": round(s2c, 4), "reachable": True,
                             "runtime_keep_x_mean": round(float(np.mean(kx_l)), 4),
                             "runtime_keep_s_mean": round(float(np.mean(ks_l)), 4),
                             "runtime_effective_mean": round(e_run, 4),
