@@ -111,6 +111,7 @@ Stage1Args stage1_args(const Plan& p, const prox_layer* L, const void* x, float 
   a.s_tilde = s_tilde;
   a.in_count = in_count;
   a.act = L->activation;
+  a.nt = 1;
   return a;
 }
 
@@ -154,6 +155,52 @@ DownArgs down_args(const Plan& p, const prox_layer* L, void* ws, const int* mask
   return a;
 }
 
+UpGateBatchArgs upgate_batch_args(const Plan& p, const prox_layer* L, const void* x, void* ws, int nt,
+                                  int* mask_idx, int* mask_count) {
+  UpGateBatchArgs a;
+  a.d = p.d;
+  a.f = p.f;
+  a.nt = nt;
+  a.act = L->activation;
+  a.w_upgate_t = L->w_upgate_t;
+  a.x = x;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.tok_bytes = p.tok_bytes;
+  a.off_bitmap = p.off_bitmap;
+  a.off_ssp = p.off_ssp;
+  a.off_ulist = p.off_ulist;
+  a.mask_idx = mask_idx;
+  a.mask_count = mask_count;
+  return a;
+}
+
+DownBatchArgs down_batch_args(const Plan& p, const prox_layer* L, void* ws, int nt) {
+  DownBatchArgs a;
+  a.d = p.d;
+  a.f = p.f;
+  a.nt = nt;
+  a.col_slices = p.dnb_col_slices;
+  a.groups = p.dnb_groups;
+  a.max_rows = p.dnb_max_rows;
+  a.w_down = L->w_down;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.tok_bytes = p.tok_bytes;
+  a.off_ssp = p.off_ssp;
+  a.off_ulist = p.off_ulist;
+  a.off_dpart = p.off_dpart;
+  return a;
+}
+
+// Token groups of the batched kernels: [g0, g0 + nt) with nt <= kBatchMax.
+template <typename Fn>
+hipError_t for_each_group(int32_t batch, Fn fn) {
+  for (int g0 = 0; g0 < batch; g0 += kBatchMax) {
+    const hipError_t e = fn(g0, std::min<int>(kBatchMax, batch - g0));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, float tau_x,
                         float tau_s, float* y, int32_t* mask_idx, int32_t* mask_count,
                         int32_t* in_count, void* ws, size_t ws_bytes, void* stream,
@@ -174,28 +221,59 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
     for (int i = 0; i < 4; ++i)
       if (!events[i]) return fail(PROX_ERR_INVALID_ARG, "events[%d] is NULL", i);
   }
-  if (stages < 1 || stages > 7)
-    return fail(PROX_ERR_INVALID_ARG, "stages %d is not a non-empty subset of 1|2|4", stages);
+  if ((stages & 7) == 0 || stages < 0 || stages > 15)
+    return fail(PROX_ERR_INVALID_ARG, "stages %d is not a non-empty subset of 1|2|4 (plus 8)", stages);
+  // batch >= 2: groups of up to kBatchMax tokens read each proxy row and each
+  // channel of the union once (Stage 2 on the matrix cores for bf16 weights)
+  // unless PROX_STAGE_PER_TOKEN asks for the per-token kernels
+  const bool grouped = batch >= 2 && !(stages & PROX_STAGE_PER_TOKEN);
+  const bool grouped_s2 = grouped && layer->wdtype == PROX_BF16;
+  const size_t es = elem_size(layer->wdtype);
+  auto x_at = [&](int g0) { return static_cast<const uint8_t*>(x) + static_cast<size_t>(g0) * p.d * es; };
+  auto ws_at = [&](int g0) { return static_cast<uint8_t*>(ws) + static_cast<size_t>(g0) * p.tok_bytes; };
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   if (stages & PROX_STAGE_PROXY) {
-    e = launch_stage1(stage1_args(p, layer, x, tau_x, tau_s, ws, nullptr, in_count), layer->wdtype,
-                      batch, false, s);
+    if (grouped) {
+      e = for_each_group(batch, [&](int g0, int nt) {
+        Stage1Args a1 = stage1_args(p, layer, x_at(g0), tau_x, tau_s, ws_at(g0), nullptr,
+                                    in_count ? in_count + g0 : nullptr);
+        a1.nt = nt;
+        return launch_stage1_batch(a1, layer->wdtype, false, s);
+      });
+    } else {
+      e = launch_stage1(stage1_args(p, layer, x, tau_x, tau_s, ws, nullptr, in_count), layer->wdtype,
+                        batch, false, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
   }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   if (stages & PROX_STAGE_UPGATE) {
-    e = launch_upgate(upgate_args(p, layer, x, ws, mask_idx, mask_count, y), layer->wdtype, batch,
-                      p.ug_blocks, true, s);
+    if (grouped_s2) {
+      e = for_each_group(batch, [&](int g0, int nt) {
+        return launch_upgate_batch(upgate_batch_args(p, layer, x_at(g0), ws_at(g0), nt,
+                                                     mask_idx + static_cast<size_t>(g0) * p.f, mask_count + g0),
+                                   s);
+      });
+    } else {
+      e = launch_upgate(upgate_args(p, layer, x, ws, mask_idx, mask_count, y), layer->wdtype, batch,
+                        p.ug_blocks, true, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "stage-2 up/gate launch");
   }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[2]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   if (stages & PROX_STAGE_DOWN) {
-    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, true, s);
+    if (grouped_s2) {
+      e = for_each_group(batch, [&](int g0, int nt) {
+        return launch_down_batch(down_batch_args(p, layer, ws_at(g0), nt), y + static_cast<size_t>(g0) * p.d, s);
+      });
+    } else {
+      e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, true, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
   }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[3]), s)) != hipSuccess)
@@ -378,6 +456,14 @@ Plan make_plan(int d, int f, int wdtype) {
   rg = (f + p.dn_chan_per_group - 1) / p.dn_chan_per_group;
   p.dn_row_groups = rg;
   p.dn_max_rows = std::max((f + rg - 1) / rg, p.dn_chan_per_group);
+  // batched down: 512-column slices, about 256 blocks; a group holds at most
+  // 2048 union ordinals (LDS)
+  p.dnb_col_slices = (d + 511) / 512;
+  int gb = (256 + p.dnb_col_slices - 1) / p.dnb_col_slices;
+  gb = std::max(gb, (f + 2047) / 2048);
+  gb = std::max(1, std::min(gb, f / 32));
+  p.dnb_groups = gb;
+  p.dnb_max_rows = ((f + gb - 1) / gb + 31) / 32 * 32;
   // per-token workspace slice
   size_t off = 0;
   p.off_tickets = off;
@@ -390,6 +476,10 @@ Plan make_plan(int d, int f, int wdtype) {
   off = align256(off + static_cast<size_t>(f / 32) * 4);
   p.off_ssp = off;
   off = align256(off + static_cast<size_t>(f) * 4);
+  p.off_ulist = off;
+  off = align256(off + static_cast<size_t>(f + 64) * 4);
+  p.off_dpart = off;
+  off = align256(off + static_cast<size_t>(p.dnb_groups) * d * 4);
   p.tok_bytes = off;
   return p;
 }
@@ -731,8 +821,21 @@ PROX_API prox_status prox_proxy_state(const prox_layer* layer, const void* x, in
       return fail(PROX_ERR_INVALID_ARG, "x must be 16-byte aligned, outputs 4-byte aligned");
     const Plan p = make_plan(layer->d_model, layer->d_ff, layer->wdtype);
     if ((st = check_ws(p, batch, ws, ws_bytes)) != PROX_OK) return st;
-    hipError_t e = launch_stage1(stage1_args(p, layer, x, tau_x, INFINITY, ws, s_tilde, in_count),
-                                 layer->wdtype, batch, true, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (batch >= 2) {  // the grouped kernel, as prox_ffn_decode runs it
+      const size_t es = elem_size(layer->wdtype);
+      e = for_each_group(batch, [&](int g0, int nt) {
+        Stage1Args a1 = stage1_args(p, layer, static_cast<const uint8_t*>(x) + static_cast<size_t>(g0) * p.d * es,
+                                    tau_x, INFINITY, static_cast<uint8_t*>(ws) + static_cast<size_t>(g0) * p.tok_bytes,
+                                    s_tilde + static_cast<size_t>(g0) * p.f, in_count ? in_count + g0 : nullptr);
+        a1.nt = nt;
+        return launch_stage1_batch(a1, layer->wdtype, true, s);
+      });
+    } else {
+      e = launch_stage1(stage1_args(p, layer, x, tau_x, INFINITY, ws, s_tilde, in_count), layer->wdtype, batch,
+                        true, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
     return PROX_OK;
   } catch (...) {

@@ -17,6 +17,7 @@ constexpr int kStage1Unroll = 16;      // proxy rows loaded per lane per batch
 constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads)
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
 constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column slice
+constexpr int kBatchMax = 8;           // tokens per group of the batched kernels
 
 // ---------------------------------------------------------------------------
 // Per-launch plan (host-computed, passed by value to kernels)
@@ -37,9 +38,15 @@ struct Plan {
   int dn_row_groups;
   int dn_max_rows;   // max rows per group (list mode) / LDS rows
   int dn_chan_per_group;  // decode mode: channels per row group (multiple of 32, <= 1024)
+  // batched down (groups of 2..8 tokens): 512-column slices x groups of union ordinals
+  int dnb_col_slices;
+  int dnb_groups;
+  int dnb_max_rows;  // rows per group, multiple of 32
   // workspace layout, bytes per token and offsets inside a token's slice
   size_t tok_bytes;
   size_t off_tickets, off_kcount, off_partial, off_bitmap, off_ssp;
+  size_t off_ulist;  // group's first token: union channel list [f] + count at [f]
+  size_t off_dpart;  // batched down partials [dnb_groups][d] fp32
 };
 
 Plan make_plan(int d, int f, int wdtype);
@@ -55,6 +62,26 @@ struct Stage1Args {
   float* s_tilde;         // [batch][f] or nullptr
   int* in_count;          // [batch] or nullptr
   int act;                // prox_activation
+  int nt;                 // batched kernel: tokens in the group (2..8)
+};
+
+// Batched Stage 2 (bf16 weights), one group of nt <= kBatchMax tokens; ws is
+// the group's first token slice, token t's slice is ws + t * tok_bytes.
+struct UpGateBatchArgs {
+  int d, f, nt, act;
+  const void* w_upgate_t;  // [f][2][d] bf16
+  const void* x;           // [nt][d] bf16
+  uint8_t* ws;
+  size_t tok_bytes, off_bitmap, off_ssp, off_ulist;
+  int* mask_idx;           // [nt][f]
+  int* mask_count;         // [nt]
+};
+
+struct DownBatchArgs {
+  int d, f, nt, col_slices, groups, max_rows;
+  const void* w_down;      // [f][d] bf16
+  uint8_t* ws;
+  size_t tok_bytes, off_ssp, off_ulist, off_dpart;
 };
 
 struct UpGateArgs {
@@ -86,6 +113,10 @@ hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_
 hipError_t launch_upgate(const UpGateArgs& a, int wdtype, int batch, int blocks,
                          bool from_bitmap, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, int wdtype, int batch, bool from_bitmap, hipStream_t s);
+hipError_t launch_stage1_batch(const Stage1Args& a, int wdtype, bool write_state, hipStream_t s);
+hipError_t launch_upgate_batch(const UpGateBatchArgs& a, hipStream_t s);
+hipError_t launch_down_batch(const DownBatchArgs& a, float* y, hipStream_t s);
+size_t down_batch_smem(const DownBatchArgs& a);
 int proxy_row_stride(int f);
 hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int qstride, int wdtype,
                        uint8_t* proxy_q, float* proxy_scale, void* w_upgate_t, hipStream_t s);

@@ -1,0 +1,404 @@
+// Stage 2 of the Prox decode step for a group of 2..8 tokens on gfx950 (bf16
+// weights): exact up/gate projections of the union of the tokens' kept
+// channels, and the down projection, on the matrix cores.
+//
+// Method ([blog] = deep-dive blog "Prox 完全拆解", section "Stage 2"), per
+// token b: s_b,j = u_b,j * act(g_b,j) for j in the token's channel list J_b
+// (dense x_b, original weights), y_b = sum_{j in J_b} s_b,j W_down[j, :].
+// A group reads each channel of the union of the J_b once; s_b,j is set to 0
+// for a token that does not keep j, so each y_b sums exactly its own J_b.
+//
+// gfx950 design:
+//   * upgate_batch_kernel: every block turns the tokens' Stage-1 bitmaps into
+//     the union channel list and the per-token index lists (block scans of
+//     the popcounts) for its slice of 16 union ordinals; two waves per 8
+//     channels split d in halves.  v_mfma_f32_16x16x32_bf16: A rows are the
+//     tokens' x (rows 8..15 zero), B columns are the up rows (0..7) and the
+//     gate rows (8..15) of the 8 channels, loaded straight from W^T (the
+//     contraction runs along a row, so each lane's 8 k-values are 16
+//     contiguous bytes).  A DPP rotate by 8 lanes brings g next to u.
+//   * down_batch_kernel: a block owns a 512-column slice and a group of union
+//     ordinals; 32-row tiles of W_down (1 KB per row) are staged in LDS and
+//     ds_read_b64_tr_b16 turns them into B operands (8 rows of one column per
+//     lane).  A rows are (token, part): s split into a bf16 high and low part
+//     (~16 significant bits; products exact, fp32 accumulation).  Each block
+//     writes its partial y; down_reduce_kernel adds the groups in fixed order,
+//     so y is reproducible bit for bit.
+#include "prox_device.h"
+#include "prox_internal.h"
+
+namespace prox {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kUgbChannels = 16;    // union channels per up/gate block
+constexpr int kUgbUnroll = 8;       // K-steps (32 elements) in flight per wave
+constexpr int kMaxWords = 8;        // bitmap words per thread (d_ff <= 65536)
+constexpr int kDnbThreads = 512;    // down: 8 waves x 64 columns
+constexpr int kDnbCols = 512;       // down: columns per block
+constexpr int kDnbTileRows = 32;    // down: rows per K-tile
+constexpr int kDnbPrefetch = 4;     // down: tiles in flight per thread
+// Every MFMA starts from zero and its result is added to the fp32 accumulator
+// with a VALU add: the matrix core aligns the products (and the accumulator
+// operand) to the largest term, so feeding it a large running sum would cost
+// the small products bits.
+constexpr f32x4_t kZero4 = {0.f, 0.f, 0.f, 0.f};
+
+// bf16 round-to-nearest-even of a finite fp32 value
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// up/gate
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs a) {
+  __shared__ int s_scan[4][1 + kBatchMax];
+  __shared__ int s_ch[kUgbChannels];
+  __shared__ uint32_t s_tb[kUgbChannels];
+  __shared__ float s_red[2][64][4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int d = a.d;
+  const int f = a.f;
+  const int nt = a.nt;
+  const int nw = f / 32;
+  const int per = (nw + kThreads - 1) / kThreads;
+  const int w0 = min(nw, tid * per);
+
+  // ---- union and per-token counts of this thread's bitmap words
+  uint32_t uw[kMaxWords];
+  int cnt[1 + kBatchMax];
+#pragma unroll
+  for (int q = 0; q <= kBatchMax; ++q) cnt[q] = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxWords; ++k) uw[k] = 0u;
+#pragma unroll
+  for (int t = 0; t < kBatchMax; ++t) {
+    if (t >= nt) break;
+    const uint32_t* bm = reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_bitmap);
+    uint32_t wv[kMaxWords];
+#pragma unroll
+    for (int k = 0; k < kMaxWords; ++k) wv[k] = bm[min(w0 + k, nw - 1)];
+#pragma unroll
+    for (int k = 0; k < kMaxWords; ++k) {
+      const uint32_t v = (k < per && w0 + k < nw) ? wv[k] : 0u;
+      uw[k] |= v;
+      cnt[1 + t] += __popc(v);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxWords; ++k) cnt[0] += __popc(uw[k]);
+
+  // ---- block scan of the 1 + nt counts (exclusive prefix per thread)
+  int inc[1 + kBatchMax];
+#pragma unroll
+  for (int q = 0; q <= kBatchMax; ++q) inc[q] = cnt[q];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+    for (int q = 0; q <= kBatchMax; ++q) {
+      const int y = __shfl_up(inc[q], o, 64);
+      if (lane >= o) inc[q] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int q = 0; q <= kBatchMax; ++q) s_scan[wave][q] = inc[q];
+  }
+  __syncthreads();
+  int excl[1 + kBatchMax], total[1 + kBatchMax];
+#pragma unroll
+  for (int q = 0; q <= kBatchMax; ++q) {
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_scan[w][q];
+    excl[q] = base + inc[q] - cnt[q];
+    total[q] = (s_scan[0][q] + s_scan[1][q]) + (s_scan[2][q] + s_scan[3][q]);
+  }
+  const int U = total[0];
+  int* ulist = reinterpret_cast<int*>(a.ws + a.off_ulist);
+  if (blockIdx.x == 0 && tid == 0) {
+    ulist[f] = U;
+    for (int t = 0; t < nt; ++t) a.mask_count[t] = total[1 + t];
+  }
+  const int u0 = static_cast<int>(blockIdx.x) * kUgbChannels;
+  if (u0 >= U) return;  // block-uniform
+  const int u1 = min(U, u0 + kUgbChannels);
+  const int nloc = u1 - u0;
+
+  // ---- the slice's channels, their token bits and the index-list entries
+  if (excl[0] < u1 && excl[0] + cnt[0] > u0) {
+    int o = excl[0];
+    int ot[kBatchMax];
+#pragma unroll
+    for (int t = 0; t < kBatchMax; ++t) ot[t] = excl[1 + t];
+    for (int k = 0; k < per && w0 + k < nw; ++k) {
+      const int w = w0 + k;
+      uint32_t tw[kBatchMax];
+#pragma unroll
+      for (int t = 0; t < kBatchMax; ++t)
+        tw[t] = t < nt ? reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(t) * a.tok_bytes +
+                                                           a.off_bitmap)[w]
+                       : 0u;
+      uint32_t bits = uw[k];
+      if (o < u1 && o + __popc(bits) > u0) {
+        while (bits) {
+          const int bit = __ffs(bits) - 1;
+          bits &= bits - 1u;
+          if (o >= u0 && o < u1) {
+            const int j = w * 32 + bit;
+            const uint32_t below = (1u << bit) - 1u;
+            uint32_t tb = 0u;
+#pragma unroll
+            for (int t = 0; t < kBatchMax; ++t) {
+              if ((tw[t] >> bit) & 1u) {
+                tb |= 1u << t;
+                a.mask_idx[static_cast<size_t>(t) * f + ot[t] + __popc(tw[t] & below)] = j;
+              }
+            }
+            s_ch[o - u0] = j;
+            s_tb[o - u0] = tb;
+            ulist[o] = j;
+          }
+          ++o;
+        }
+      } else {
+        o += __popc(bits);
+      }
+#pragma unroll
+      for (int t = 0; t < kBatchMax; ++t) ot[t] += __popc(tw[t]);
+    }
+  }
+  __syncthreads();
+
+  // ---- MFMA: wave -> (channel half ch = wave & 1, K half kh = wave >> 1)
+  const int chh = wave & 1;
+  const int kh = wave >> 1;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int slot = chh * 8 + (n & 7);
+  const int j = s_ch[min(slot, nloc - 1)];
+  typedef uint16_t S;
+  const S* wrow = static_cast<const S*>(a.w_upgate_t) + (static_cast<size_t>(j) * 2 + (n >= 8 ? 1 : 0)) * d;
+  const int m = lane & 15;  // A row = token
+  const S* xrow = static_cast<const S*>(a.x) + static_cast<size_t>(min(m, nt - 1)) * d;
+  const bool xon = m < nt;
+  const int half = d / 2;
+  const int kbeg = kh * half + 8 * g;
+  const int nsteps = half / 32;
+  f32x4_t C = {0.f, 0.f, 0.f, 0.f};
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  for (int s0 = 0; s0 < nsteps; s0 += kUgbUnroll) {
+    u32x4_t bw[kUgbUnroll], ax[kUgbUnroll];
+#pragma unroll
+    for (int u = 0; u < kUgbUnroll; ++u) {
+      const int k = kbeg + 32 * min(s0 + u, nsteps - 1);
+      bw[u] = *reinterpret_cast<const u32x4_t*>(wrow + k);
+      ax[u] = xon ? *reinterpret_cast<const u32x4_t*>(xrow + k) : z;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kUgbUnroll; ++u) {
+      if (s0 + u < nsteps)  // wave-uniform; see the note on kZero4
+        C += __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u]),
+                                                     __builtin_bit_cast(bf16x8_t, bw[u]), kZero4, 0, 0, 0);
+    }
+  }
+  // ---- add the two K halves, then s = u * act(g) for the tokens that keep j
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[chh][lane][i] = C[i];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) C[i] += s_red[chh][lane][i];
+  float gt[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)  // lane n < 8 receives lane n + 8 (gate of the same channel)
+    gt[i] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(C[i]), 0x128, 0xF, 0xF, false));
+  if (n < 8 && g < 2 && slot < nloc) {
+    const uint32_t tb = s_tb[slot];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * g + i;
+      if (t < nt) {
+        float* ssp = reinterpret_cast<float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_ssp);
+        ssp[j] = ((tb >> t) & 1u) ? C[i] * gate_act(gt[i], a.act) : 0.f;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kDnbThreads) void down_batch_kernel(DownBatchArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int d = a.d;
+  const int f = a.f;
+  const int nt = a.nt;
+  const int cs = static_cast<int>(blockIdx.x) % a.col_slices;
+  const int gi = static_cast<int>(blockIdx.x) / a.col_slices;
+  const int* ulist = reinterpret_cast<const int*>(a.ws + a.off_ulist);
+  const int U = min(max(ulist[f], 0), f);
+  const int o0 = static_cast<int>(static_cast<long long>(U) * gi / a.groups);
+  const int o1 = static_cast<int>(static_cast<long long>(U) * (gi + 1) / a.groups);
+  const int nr = o1 - o0;  // <= a.max_rows
+  const int ntile = (nr + kDnbTileRows - 1) / kDnbTileRows;
+
+  // LDS: staged W tiles [2][32][512] bf16, A tiles [max_rows/32][4][16][8] bf16, rows' channels
+  uint16_t* wb = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* As = wb + 2 * kDnbTileRows * kDnbCols;
+  int* ul = reinterpret_cast<int*>(As + static_cast<size_t>(a.max_rows) * 16);
+  for (int r = tid; r < nr; r += kDnbThreads) ul[r] = min(max(ulist[o0 + r], 0), f - 1);
+  __syncthreads();
+  // A: rows r of the group, m = 2t + part: s_t[ul[r]] split into bf16 hi and lo
+  for (int idx = tid; idx < ntile * kDnbTileRows * kBatchMax; idx += kDnbThreads) {
+    const int r = idx / kBatchMax;
+    const int t = idx % kBatchMax;
+    float s = 0.f;
+    if (r < nr && t < nt)
+      s = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_ssp)[ul[r]];
+    const uint16_t hi = f32_to_bf16_rne(s);
+    const uint16_t lo = f32_to_bf16_rne(s - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+    const int kt = r / kDnbTileRows;
+    const int k = r % kDnbTileRows;
+    uint16_t* at = As + static_cast<size_t>(kt) * 512 + ((k >> 3) * 16) * 8 + (k & 7);
+    at[(2 * t) * 8] = hi;
+    at[(2 * t + 1) * 8] = lo;
+  }
+
+  // staging: thread -> (16-B unit u = tid % 64, rows tid / 64 + 8q); unit u of
+  // row r sits at unit u ^ (2 * (r & 3)) (conflict-free transposed reads)
+  const int unit = tid & 63;
+  const int col0 = cs * kDnbCols;
+  const bool col_ok = col0 + unit * 8 < d;
+  const uint16_t* W = static_cast<const uint16_t*>(a.w_down);
+  u32x4_t ld[kDnbPrefetch][4];
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  auto issue = [&](int kt, u32x4_t (&dst)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = kt * kDnbTileRows + (tid >> 6) + 8 * q;
+      const int ch = ul[min(r, nr - 1)];
+      dst[q] = col_ok ? *reinterpret_cast<const u32x4_t*>(W + static_cast<size_t>(ch) * d + col0 + unit * 8) : z;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < kDnbPrefetch; ++p)
+    if (p < ntile) issue(p, ld[p]);
+  __syncthreads();  // A complete
+
+  const int g = lane >> 4;
+  const int jq = lane & 15;
+  const int ri = jq >> 2;  // row within the 4-row transposed read
+  const int qq = jq & 3;   // 4-column group within the 16-column tile
+  const int m = lane & 15;
+  const bool wave_on = col0 + 64 * wave < d;  // d % 64 == 0
+  f32x4_t C[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) C[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int kt0 = 0; kt0 < ntile; kt0 += kDnbPrefetch) {
+#pragma unroll
+    for (int p = 0; p < kDnbPrefetch; ++p) {
+      const int kt = kt0 + p;
+      if (kt >= ntile) break;  // block-uniform
+      uint16_t* buf = wb + (kt & 1) * kDnbTileRows * kDnbCols;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = (tid >> 6) + 8 * q;
+        *reinterpret_cast<u32x4_t*>(buf + r * kDnbCols + 8 * (unit ^ (2 * (r & 3)))) = ld[p][q];
+      }
+      if (kt + kDnbPrefetch < ntile) issue(kt + kDnbPrefetch, ld[p]);
+      __syncthreads();
+      if (wave_on) {
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(As + static_cast<size_t>(kt) * 512 + (g * 16 + m) * 8);
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) {
+          const int ut = 2 * (4 * wave + nn) + (qq >> 1);  // 16-B unit of this lane's 4 columns
+          const int r1 = 8 * g + ri;
+          const int r2 = r1 + 4;
+          const int o1 = r1 * kDnbCols + 8 * (ut ^ (2 * (r1 & 3))) + 4 * (qq & 1);
+          const int o2 = r2 * kDnbCols + 8 * (ut ^ (2 * (r2 & 3))) + 4 * (qq & 1);
+          const bf16x4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4_t*)((__attribute__((address_space(3))) uint16_t*)(buf) + o1));
+          const bf16x4_t b2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4_t*)((__attribute__((address_space(3))) uint16_t*)(buf) + o2));
+          const bf16x8_t bv = {b1[0], b1[1], b1[2], b1[3], b2[0], b2[1], b2[2], b2[3]};
+          C[nn] += __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, kZero4, 0, 0, 0);
+        }
+      }
+      // the buffer written two tiles later is the one just read: every wave
+      // passes the next iteration's barrier before that write
+    }
+  }
+  // ---- partial y of this group: lane (g, n) holds tokens 2g, 2g+1 of column n
+  if (wave_on) {
+    const int n = lane & 15;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = 2 * g + tt;
+      if (t >= nt) continue;
+      float* dp = reinterpret_cast<float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_dpart) +
+                  static_cast<size_t>(gi) * d;
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn)
+        dp[col0 + 64 * wave + 16 * nn + n] = C[nn][2 * tt] + C[nn][2 * tt + 1];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void down_reduce_kernel(DownBatchArgs a, float* y) {
+  const int idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= a.nt * a.d) return;
+  const int t = idx / a.d;
+  const int c = idx - t * a.d;
+  const float* dp = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_dpart) + c;
+  float s = 0.f;
+  for (int g0 = 0; g0 < a.groups; g0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = dp[static_cast<size_t>(min(g0 + u, a.groups - 1)) * a.d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (g0 + u < a.groups) s += v[u];
+  }
+  y[idx] = s;
+}
+
+}  // namespace
+
+size_t down_batch_smem(const DownBatchArgs& a) {
+  return static_cast<size_t>(2) * kDnbTileRows * kDnbCols * 2 + static_cast<size_t>(a.max_rows) * 16 * 2 +
+         static_cast<size_t>(a.max_rows) * 4;
+}
+
+hipError_t launch_upgate_batch(const UpGateBatchArgs& a, hipStream_t s) {
+  const int blocks = (a.f + kUgbChannels - 1) / kUgbChannels;
+  hipLaunchKernelGGL(upgate_batch_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_batch(const DownBatchArgs& a, float* y, hipStream_t s) {
+  hipLaunchKernelGGL(down_batch_kernel, dim3(static_cast<unsigned>(a.col_slices * a.groups)), dim3(kDnbThreads),
+                     down_batch_smem(a), s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = a.nt * a.d;
+  hipLaunchKernelGGL(down_reduce_kernel, dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, s, a, y);
+  return hipGetLastError();
+}
+
+}  // namespace prox

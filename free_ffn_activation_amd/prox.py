@@ -28,6 +28,7 @@ PROX_ACT_GELU_TANH = 1
 PROX_STAGE_PROXY = 1
 PROX_STAGE_UPGATE = 2
 PROX_STAGE_DOWN = 4
+PROX_STAGE_PER_TOKEN = 8  # batch >= 2: per-token kernels instead of the grouped ones
 
 _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPORTED",
                  -3: "PROX_ERR_HIP", -4: "PROX_ERR_INTERNAL"}

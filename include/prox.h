@@ -214,7 +214,16 @@ prox_status prox_calibrate_hist(const prox_layer* layer, const void* X_cal, int3
  *   mask_count  device [batch] int32 (k_s per token)
  *   in_count    device [batch] int32 (k_x per token) or NULL
  *   ws          device, >= prox_workspace_size(batch) bytes, zeroed once
- * Asynchronous: three kernels on `stream`, no host synchronisation.
+ * Asynchronous: kernels on `stream`, no host synchronisation.  batch 1 runs
+ * three kernels.  batch >= 2 runs groups of up to 8 tokens (the pages study
+ * batch 1 and leave larger batches open, [blog] limitations section): Stage 1
+ * reads each proxy row of the union of the group's kept input rows once and
+ * gives a token a zero weight on the rows it rejects; for bf16 weights Stage 2
+ * reads each channel of the union of the group's channel lists once (s = 0
+ * for a token that drops the channel) and adds the down projection's partial
+ * sums in fixed order, so y is reproducible bit for bit; fp32 layers run
+ * Stage 2 per token.  Every token's masks, k_x, k_s and y follow the batch-1
+ * definition.
  */
 prox_status prox_ffn_decode(const prox_layer* layer, const void* x, int32_t batch,
                             float tau_x, float tau_s, float* y, int32_t* mask_idx,
@@ -237,7 +246,8 @@ prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32
  *               channel bitmap in ws, in_count), PROX_STAGE_UPGATE (channel
  *               list from the bitmap -> mask_idx, mask_count; s_j in ws; zeroes
  *               y), PROX_STAGE_DOWN (accumulates y from mask_idx, mask_count and
- *               the s_j in ws).  7 is prox_ffn_decode.
+ *               the s_j in ws; the grouped bf16 path at batch >= 2 instead
+ *               writes y from its partial sums).  7 is prox_ffn_decode.
  * A stage run without its predecessors reads what an earlier call with the
  * same layer, x, thresholds, outputs and workspace left there.  Other
  * arguments as prox_ffn_decode.  Asynchronous.
@@ -245,6 +255,10 @@ prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32
 #define PROX_STAGE_PROXY 1
 #define PROX_STAGE_UPGATE 2
 #define PROX_STAGE_DOWN 4
+/* with batch >= 2: run the per-token kernels (each token reads its own rows
+ * and channels) instead of the grouped ones; same results up to fp32
+ * summation order */
+#define PROX_STAGE_PER_TOKEN 8
 prox_status prox_ffn_decode_stages(const prox_layer* layer, const void* x, int32_t batch,
                                    float tau_x, float tau_s, float* y, int32_t* mask_idx,
                                    int32_t* mask_count, int32_t* in_count, void* ws,
@@ -264,7 +278,8 @@ prox_status prox_ffn_stage2(const prox_layer* layer, const void* x, int32_t batc
 
 /*
  * Stage 1 alone: the proxy state s~ ([blog] "Stage 1", equations for u~, h~,
- * s~) for every channel.
+ * s~) for every channel.  batch >= 2 runs the grouped Stage-1 kernel, as
+ * prox_ffn_decode does, so s~ is what the decode thresholds.
  *   s_tilde     device [batch][d_ff] fp32
  *   in_count    device [batch] int32 or NULL
  * Asynchronous.

@@ -134,6 +134,6 @@ def test_other_entry_points_validate():
     assert lib.prox_calibrate_hist(ctypes.byref(L), FAKE, 64, 0.5, 1.5, 200000, 4096, ctypes.byref(tx),
                                    ctypes.byref(ts), FAKE, 1 << 30, None) == P.PROX_ERR_INVALID_ARG
     # stage subsets must be a non-empty subset of the three kernels
-    for bad in (0, 8, -1):
+    for bad in (0, 8, 16, 24, -1):
         assert lib.prox_ffn_decode_stages(ctypes.byref(L), FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE,
                                           None, FAKE, 1 << 30, None, bad) == P.PROX_ERR_INVALID_ARG
