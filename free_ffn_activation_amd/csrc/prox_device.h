@@ -60,17 +60,53 @@ template <> __device__ __forceinline__ float dot16<F32Tag>(uint4 w, uint4 x, flo
   return acc;
 }
 
-// Sum over the 64 lanes of a wave; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+// Inclusive prefix sums over the 64 lanes of a wave with DPP (VALU only, no
+// LDS round trips): row shifts by 1, 2, 4, 8 give prefix sums within each row
+// of 16 lanes (a source lane outside the row reads 0), then row broadcasts of
+// lane 15 and lane 31 carry the earlier rows' totals forward.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));  // row_shr:1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));  // row_shr:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));  // row_shr:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));  // row_shr:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
   return v;
 }
 
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+__device__ __forceinline__ int wave_inclusive_scan_int(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the total (lane 63 of
+// the inclusive scan).
+__device__ __forceinline__ float wave_sum(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_inclusive_scan(v)), 63));
+}
+
+// Maximum over the 64 lanes of a wave of non-negative floats, returned to
+// every lane: DPP row shifts give each row's maximum in its lane 15, two row
+// broadcasts carry it to lane 63 (VALU only, no LDS round trips).  Lanes whose
+// DPP source is outside the row read 0, the identity for non-negative values.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  int x = __float_as_int(v);  // non-negative floats order like their bits
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false));  // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false));  // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false));  // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false));  // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+  return __builtin_amdgcn_readlane(wave_inclusive_scan_int(v), 63);
 }
 
 // SiLU(z) = z / (1 + e^{-z}); e^{-z} overflowing to +inf gives -0 as required.

@@ -99,15 +99,7 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
   // ---- block scan of the 1 + nt counts (exclusive prefix per thread)
   int inc[1 + kBatchMax];
 #pragma unroll
-  for (int q = 0; q <= kBatchMax; ++q) inc[q] = cnt[q];
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-    for (int q = 0; q <= kBatchMax; ++q) {
-      const int y = __shfl_up(inc[q], o, 64);
-      if (lane >= o) inc[q] += y;
-    }
-  }
+  for (int q = 0; q <= kBatchMax; ++q) inc[q] = wave_inclusive_scan_int(cnt[q]);
   if (lane == 63) {
 #pragma unroll
     for (int q = 0; q <= kBatchMax; ++q) s_scan[wave][q] = inc[q];

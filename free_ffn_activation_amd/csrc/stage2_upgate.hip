@@ -35,12 +35,7 @@ constexpr int kMaxWordsPerThread = 8;
 __device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_scan_int(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   int base = 0;
