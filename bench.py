@@ -118,6 +118,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-budget", action="store_true",
                     help="skip the computation-budget operating points")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="skip the batch-8 decode (grouped kernels vs per-token kernels vs dense)")
     ap.add_argument("--pmc-copy-mib", type=int, default=0,
                     help="only run device copies of this many MiB (counter scale reference)")
     return ap.parse_args()
@@ -568,6 +570,114 @@ def main() -> int:
                  "mean_k_x": round(sched_mean(kx_g), 1), "mean_k_s": round(sched_mean(ks_g), 1)}
         del gws
 
+    # ---------------------------------------------------------------- batch 8
+    # Eight independent tokens per step through one layer (each token its own
+    # masks): the rotation's layers with their 16 tokens taken 8 at a time.
+    # Timed three ways on the same schedule: the grouped kernels (union of the
+    # tokens' rows and channels read once), the per-token kernels
+    # (PROX_STAGE_PER_TOKEN: each token reads its own), torch's dense bf16 FFN
+    # at M = 8.  Required bytes use the union counts: K_x^U * d_ff + 8 K_x^U +
+    # 3 K_s^U * d * 2 + 8 (2d + 4d) + 4 sum(k_s).
+    batch8 = None
+    if not args.no_batch and n_tok % 8 == 0:
+        B = 8
+        nb = n_tok // B
+        sched_b = [(s % n_layers, (s // n_layers) % nb) for s in range(n_layers * nb)]
+        xbt = [[x_all[l, B * h:B * h + B] for h in range(nb)] for l in range(n_layers)]
+        by8 = torch.empty(B, d, dtype=torch.float32, device=dev)
+        bmi8 = torch.empty(B, f, dtype=torch.int32, device=dev)
+        bmc8 = torch.empty(B, dtype=torch.int32, device=dev)
+        bic8 = torch.empty(B, dtype=torch.int32, device=dev)
+        bws8 = prox.new_workspace(d, f, B)
+        kxu = np.zeros((n_layers, nb), np.int64)
+        ksu = np.zeros((n_layers, nb), np.int64)
+        ks_sum = np.zeros((n_layers, nb), np.int64)
+        kx_tok = np.zeros((n_layers, nb), np.float64)
+        for l in range(n_layers):
+            tx, ts = taus[l]
+            for h in range(nb):
+                prox.prox_ffn_decode(layers[l], xbt[l][h], tx, ts, by8, bmi8, bmc8, bic8, bws8)
+                torch.cuda.synchronize()
+                xv = xbt[l][h].view(torch.bfloat16).float().abs()
+                kxu[l, h] = int((xv >= tx).any(dim=0).sum().item())
+                cnt = bmc8.cpu().numpy()
+                um = torch.zeros(f, dtype=torch.bool, device=dev)
+                for k in range(B):
+                    um[bmi8[k, :int(cnt[k])].long()] = True
+                ksu[l, h] = int(um.sum().item())
+                ks_sum[l, h] = int(cnt.sum())
+                kx_tok[l, h] = float(bic8.float().mean().item())
+
+        def bmean(a):
+            return float(np.mean([a[l, h] for (l, h) in sched_b]))
+
+        breq8 = kxu * f + 8 * kxu + 3 * ksu * d * 2 + B * (2 * d + 4 * d) + 4 * ks_sum
+        by_s1 = kxu * f + 8 * kxu + B * 2 * d + B * f // 8
+        by_ug = 2 * ksu * d * 2 + B * 2 * d + 8 * ksu
+        by_dn = ksu * d * 2 + 8 * ksu + B * 4 * d
+
+        def b_step(stages):
+            def fn(s):
+                l, h = sched_b[s % len(sched_b)]
+                tx, ts = taus[l]
+                prox.prox_ffn_decode_stages(layers[l], xbt[l][h], tx, ts, by8, bmi8, bmc8, bic8, bws8, stages)
+            return fn
+
+        us_grp = time_graph(b_step(7), "batch 8, grouped kernels")[0]
+        us_pt = time_graph(b_step(7 | prox.PROX_STAGE_PER_TOKEN), "batch 8, per-token kernels")[0]
+        # each grouped kernel alone: every schedule step gets a workspace and
+        # outputs prepared by one full decode
+        nsb = len(sched_b)
+        iso8 = [(prox.new_workspace(d, f, B), torch.empty(B, d, dtype=torch.float32, device=dev),
+                 torch.empty(B, f, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                 torch.empty(B, dtype=torch.int32, device=dev)) for _ in range(nsb)]
+
+        def b_iso(stages):
+            def fn(s):
+                l, h = sched_b[s % nsb]
+                tx, ts = taus[l]
+                wsx, yx, mix, mcx, icx = iso8[s % nsb]
+                prox.prox_ffn_decode_stages(layers[l], xbt[l][h], tx, ts, yx, mix, mcx, icx, wsx, stages)
+            return fn
+
+        for s in range(nsb):
+            b_iso(7)(s)
+        torch.cuda.synchronize()
+        k8 = [time_graph(b_iso(bit), f"batch 8, {nm} alone")[0] for nm, bit in zip(names, stage_bits)]
+        dense8 = None
+        if not args.no_dense:
+            wug8 = [L.w_upgate_t.view(torch.bfloat16).view(2 * f, d) for L in layers]
+            wdn8 = [L.w_down.view(torch.bfloat16).view(f, d) for L in layers]
+            yb8 = torch.empty(B, d, dtype=torch.bfloat16, device=dev)
+
+            def dense8_fn(s):
+                l, h = sched_b[s % nsb]
+                xx = xbt[l][h].view(torch.bfloat16)
+                ug = torch.nn.functional.linear(xx, wug8[l])
+                sv = ug[:, 0::2] * torch.nn.functional.silu(ug[:, 1::2])
+                torch.matmul(sv, wdn8[l], out=yb8)
+
+            for s in range(4):
+                dense8_fn(s)
+            torch.cuda.synchronize()
+            dense8 = round(time_graph(dense8_fn, "batch 8, dense torch bf16")[0], 3)
+        mb8 = bmean(breq8)
+        bk8 = [bmean(a) for a in (by_s1, by_ug, by_dn)]
+        batch8 = {"batch": B, "us_per_step": round(us_grp, 3), "tokens_per_s": round(B / (us_grp * 1e-6), 1),
+                  "us_per_token": round(us_grp / B, 3),
+                  "required_MB_union": round(mb8 / 1e6, 3), "GBps": round(mb8 / (us_grp * 1e-6) / 1e9, 1),
+                  "pct_hbm_roofline": round(100.0 * mb8 / (us_grp * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                  "mean_K_x_union": round(bmean(kxu), 1), "mean_K_s_union": round(bmean(ksu), 1),
+                  "mean_k_x_token": round(bmean(kx_tok), 1), "mean_k_s_token": round(bmean(ks_sum) / B, 1),
+                  "per_token_kernels_us_per_step": round(us_pt, 3),
+                  "dense_torch_bf16_us_per_step": dense8,
+                  "kernels": {names[i]: {"us": round(k8[i], 3), "algorithmic_MB": round(bk8[i] / 1e6, 3),
+                                         "GBps": round(bk8[i] / (k8[i] * 1e-6) / 1e9, 1)} for i in range(3)},
+                  "schedule": f"{n_layers} layers x {nb} groups of 8 of their {n_tok} tokens"}
+        log(f"batch 8: grouped {us_grp:.2f} us/step ({mb8 / 1e6:.1f} MB union), per-token kernels {us_pt:.2f}, "
+            f"dense torch {dense8}; kernels " + ", ".join(f"{names[i]} {k8[i]:.2f}" for i in range(3)))
+        del iso8, bws8
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -631,6 +741,7 @@ def main() -> int:
         "budget": budget,
         "geglu": geglu,
         "calibration": calibration,
+        "batch8": batch8,
     }
     print(json.dumps(out), flush=True)
     return 0
