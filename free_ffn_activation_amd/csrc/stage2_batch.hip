@@ -34,8 +34,10 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-constexpr int kUgbChannels = 16;    // union channels per up/gate block
-constexpr int kUgbUnroll = 8;       // K-steps (32 elements) in flight per wave
+constexpr int kUgbChannels = 16;    // union channels per up/gate block (32 staged rows)
+constexpr int kUgbKt = 512;         // K elements per staged tile (1 KB per row)
+constexpr int kUgbRowBytes = kUgbKt * 2 + 16;  // staged row stride
+constexpr int kUgbRowsPerThread = 2 * kUgbChannels / 4;  // 32 rows over 4 waves
 constexpr int kMaxWords = 8;        // bitmap words per thread (d_ff <= 65536)
 constexpr int kDnbThreads = 512;    // down: 8 waves x 64 columns
 constexpr int kDnbCols = 512;       // down: columns per block
@@ -61,6 +63,8 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
   __shared__ int s_ch[kUgbChannels];
   __shared__ uint32_t s_tb[kUgbChannels];
   __shared__ float s_red[2][64][4];
+  __shared__ __align__(16) uint8_t s_w[2 * kUgbChannels * kUgbRowBytes];
+  __shared__ __align__(16) uint8_t s_x[16 * kUgbRowBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -177,30 +181,70 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
   const int slot = chh * 8 + (n & 7);
   const int j = s_ch[min(slot, nloc - 1)];
   typedef uint16_t S;
-  const S* wrow = static_cast<const S*>(a.w_upgate_t) + (static_cast<size_t>(j) * 2 + (n >= 8 ? 1 : 0)) * d;
-  const int m = lane & 15;  // A row = token
-  const S* xrow = static_cast<const S*>(a.x) + static_cast<size_t>(min(m, nt - 1)) * d;
-  const bool xon = m < nt;
-  const int half = d / 2;
-  const int kbeg = kh * half + 8 * g;
-  const int nsteps = half / 32;
+  // K-tiles of 512 elements are staged in LDS: each wave load instruction
+  // reads one contiguous 1 KB row segment (the DRAM-friendly pattern), and
+  // the MFMA operands are read back from LDS.  Staged row r = 16 tt + n holds,
+  // for n < 8, the up row of slot 8 tt + n and, for n >= 8, its gate row;
+  // rows are padded by 16 B so the operand reads are conflict-free.  x of the
+  // group sits in LDS rows 0..7 (rows 8..15 stay zero: the A rows past the
+  // tokens).  The next tile's loads are in flight while a tile is computed.
+  const S* W = static_cast<const S*>(a.w_upgate_t);
+  const S* X = static_cast<const S*>(a.x);
+  const int unit = tid & 63;
+  const S* wsrc[kUgbRowsPerThread];
+#pragma unroll
+  for (int q = 0; q < kUgbRowsPerThread; ++q) {
+    const int r = (tid >> 6) + 4 * q;
+    const int sl = 8 * (r >> 4) + (r & 7);
+    wsrc[q] = W + (static_cast<size_t>(s_ch[min(sl, nloc - 1)]) * 2 + ((r >> 3) & 1)) * d;
+  }
+  const int xt = tid >> 5;  // token row of this thread's x units
+  const S* xsrc = X + static_cast<size_t>(min(xt, nt - 1)) * d;
+  const bool xon = xt < nt;
+  {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < 8 * kUgbRowBytes / 16; i += kThreads)
+      *reinterpret_cast<u32x4_t*>(s_x + 8 * kUgbRowBytes + 16 * i) = z;
+  }
+  u32x4_t wv[kUgbRowsPerThread], xv[2];
+  const int nkt = (d + kUgbKt - 1) / kUgbKt;
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * kUgbKt;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const bool won = k0 + unit * 8 < d;
+#pragma unroll
+    for (int q = 0; q < kUgbRowsPerThread; ++q)
+      wv[q] = won ? *reinterpret_cast<const u32x4_t*>(wsrc[q] + k0 + unit * 8) : z;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int xu = (tid & 31) + 32 * q;
+      xv[q] = (xon && k0 + xu * 8 < d) ? *reinterpret_cast<const u32x4_t*>(xsrc + k0 + xu * 8) : z;
+    }
+  };
+  load_tile(0);
   f32x4_t C = {0.f, 0.f, 0.f, 0.f};
-  const u32x4_t z = {0u, 0u, 0u, 0u};
-  for (int s0 = 0; s0 < nsteps; s0 += kUgbUnroll) {
-    u32x4_t bw[kUgbUnroll], ax[kUgbUnroll];
+  const int m = lane & 15;  // A row = token
+  const int brow = 16 * chh + n;
+  for (int kt = 0; kt < nkt; ++kt) {
 #pragma unroll
-    for (int u = 0; u < kUgbUnroll; ++u) {
-      const int k = kbeg + 32 * min(s0 + u, nsteps - 1);
-      bw[u] = *reinterpret_cast<const u32x4_t*>(wrow + k);
-      ax[u] = xon ? *reinterpret_cast<const u32x4_t*>(xrow + k) : z;
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < kUgbRowsPerThread; ++q)
+      *reinterpret_cast<u32x4_t*>(s_w + ((tid >> 6) + 4 * q) * kUgbRowBytes + 16 * unit) = wv[q];
 #pragma unroll
-    for (int u = 0; u < kUgbUnroll; ++u) {
-      if (s0 + u < nsteps)  // wave-uniform; see the note on kZero4
-        C += __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u]),
-                                                     __builtin_bit_cast(bf16x8_t, bw[u]), kZero4, 0, 0, 0);
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<u32x4_t*>(s_x + xt * kUgbRowBytes + 16 * ((tid & 31) + 32 * q)) = xv[q];
+    __syncthreads();
+    if (kt + 1 < nkt) load_tile(kt + 1);
+    const int kvalid = min(kUgbKt, d - kt * kUgbKt);
+#pragma unroll
+    for (int s2 = 0; s2 < kUgbKt / 64; ++s2) {
+      const int st = kh * (kUgbKt / 64) + s2;  // this wave's half of the tile's K-steps
+      if (32 * st < kvalid) {  // wave-uniform
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(s_w + brow * kUgbRowBytes + 64 * st + 16 * g);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(s_x + m * kUgbRowBytes + 64 * st + 16 * g);
+        C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, C, 0, 0, 0);
+      }
     }
+    __syncthreads();  // the staged tile is rewritten next
   }
   // ---- add the two K halves, then s = u * act(g) for the tokens that keep j
   if (kh == 1) {
