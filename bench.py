@@ -61,6 +61,10 @@ KERNEL_SOURCES = {
     "stage1_proxy": "stage1.hip",
     "stage2_upgate": "stage2_upgate.hip",
     "stage2_down": "stage2_down.hip",
+    # grouped batch kernels (2..8 tokens per group)
+    "stage1_proxy_batch": "stage1_batch.hip",
+    "stage2_upgate_batch": "stage2_batch.hip",
+    "stage2_down_batch": "stage2_batch.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -663,6 +667,10 @@ def main() -> int:
             dense8 = round(time_graph(dense8_fn, "batch 8, dense torch bf16")[0], 3)
         mb8 = bmean(breq8)
         bk8 = [bmean(a) for a in (by_s1, by_ug, by_dn)]
+        names8 = [nm + "_batch" for nm in names]
+        dom8 = int(np.argmax(k8))
+        ach8 = bk8[dom8] / (k8[dom8] * 1e-6) / 1e9
+        traffic8 = measured_traffic(names8[dom8], bk8[dom8])
         batch8 = {"batch": B, "us_per_step": round(us_grp, 3), "tokens_per_s": round(B / (us_grp * 1e-6), 1),
                   "us_per_token": round(us_grp / B, 3),
                   "required_MB_union": round(mb8 / 1e6, 3), "GBps": round(mb8 / (us_grp * 1e-6) / 1e9, 1),
@@ -671,8 +679,12 @@ def main() -> int:
                   "mean_k_x_token": round(bmean(kx_tok), 1), "mean_k_s_token": round(bmean(ks_sum) / B, 1),
                   "per_token_kernels_us_per_step": round(us_pt, 3),
                   "dense_torch_bf16_us_per_step": dense8,
-                  "kernels": {names[i]: {"us": round(k8[i], 3), "algorithmic_MB": round(bk8[i] / 1e6, 3),
-                                         "GBps": round(bk8[i] / (k8[i] * 1e-6) / 1e9, 1)} for i in range(3)},
+                  "kernels": {names8[i]: {"us": round(k8[i], 3), "algorithmic_MB": round(bk8[i] / 1e6, 3),
+                                          "GBps": round(bk8[i] / (k8[i] * 1e-6) / 1e9, 1)} for i in range(3)},
+                  "roofline": {"bound": "hbm", "kernel": names8[dom8], "achieved": round(ach8, 1),
+                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach8 / HBM_PEAK_GBPS, 4),
+                               "traffic": traffic8["bytes_per_launch"] if traffic8 else None,
+                               "traffic_detail": traffic8},
                   "schedule": f"{n_layers} layers x {nb} groups of 8 of their {n_tok} tokens"}
         log(f"batch 8: grouped {us_grp:.2f} us/step ({mb8 / 1e6:.1f} MB union), per-token kernels {us_pt:.2f}, "
             f"dense torch {dense8}; kernels " + ", ".join(f"{names[i]} {k8[i]:.2f}" for i in range(3)))

@@ -461,7 +461,7 @@ Plan make_plan(int d, int f, int wdtype) {
   p.dnb_col_slices = (d + 511) / 512;
   int gb = (256 + p.dnb_col_slices - 1) / p.dnb_col_slices;
   gb = std::max(gb, (f + 2047) / 2048);
-  gb = std::max(1, std::min(gb, f / 32));
+  gb = std::max(1, std::min({gb, f / 32, 64}));  // at most 64 groups: the reduction holds one value per group
   p.dnb_groups = gb;
   p.dnb_max_rows = ((f + gb - 1) / gb + 31) / 32 * 32;
   // per-token workspace slice

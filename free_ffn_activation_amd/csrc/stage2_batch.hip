@@ -42,7 +42,8 @@ constexpr int kMaxWords = 8;        // bitmap words per thread (d_ff <= 65536)
 constexpr int kDnbThreads = 512;    // down: 8 waves x 64 columns
 constexpr int kDnbCols = 512;       // down: columns per block
 constexpr int kDnbTileRows = 32;    // down: rows per K-tile
-constexpr int kDnbPrefetch = 4;     // down: tiles in flight per thread
+constexpr int kDnbPrefetch = 2;     // down: tiles in flight per thread
+constexpr int kDnbMaxGroups = 64;   // down: groups of union ordinals (a plan bound)
 // Every MFMA starts from zero and its result is added to the fp32 accumulator
 // with a VALU add: the matrix core aligns the products (and the accumulator
 // operand) to the largest term, so feeding it a large running sum would cost
@@ -401,15 +402,16 @@ __global__ __launch_bounds__(kThreads) void down_reduce_kernel(DownBatchArgs a, 
   const int t = idx / a.d;
   const int c = idx - t * a.d;
   const float* dp = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_dpart) + c;
+  // every group's partial is in flight at once (groups <= kDnbMaxGroups);
+  // the sum keeps the fixed group order
+  float v[kDnbMaxGroups];
+#pragma unroll
+  for (int u = 0; u < kDnbMaxGroups; ++u)
+    if (u < a.groups) v[u] = dp[static_cast<size_t>(u) * a.d];
   float s = 0.f;
-  for (int g0 = 0; g0 < a.groups; g0 += 8) {
-    float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = dp[static_cast<size_t>(min(g0 + u, a.groups - 1)) * a.d];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (g0 + u < a.groups) s += v[u];
-  }
+  for (int u = 0; u < kDnbMaxGroups; ++u)
+    if (u < a.groups) s += v[u];
   y[idx] = s;
 }
 
