@@ -41,6 +41,10 @@ Readings where the pages are silent (each also listed in the design notes):
       models) use GELU in its tanh form,
       0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), in both the proxy
       state and Stage 2; everything else is unchanged.
+  R20 the pages' precision ablation swaps the INT4 proxy for an FP16 one at
+      the same budget; read as a 16-bit proxy that is the layer's own 16-bit
+      weights (bf16 for these layers), so the proxy state is the input-sparse
+      projection with the original weights and nothing is quantised.
 
 Parity pins: every function here is pinned by tests that do not route through
 itself (dense SwiGLU, brute-force sorts, closed forms, page values); the
@@ -150,6 +154,20 @@ def proxy_state(x, q_up, sc_up, q_gate, sc_gate, tau_x, act="silu"):
     return {"u": u, "g": g, "s": s, "m_x": m_x}
 
 
+def proxy_state_w16(x, W_up, W_gate, tau_x, act="silu"):
+    """Stage-1 proxy state with the 16-bit proxy of the pages' precision
+    ablation ([blog] evidence section, ablation A1; reading R20): the proxy
+    matrices are the layer's own 16-bit weights, so
+    u~ = Pi^in(x, W_up, m_x), h~ = act(Pi^in(x, W_gate, m_x)), s~ = u~ h~.
+    Returns dict(u, g, s, m_x).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m_x = input_mask(x, tau_x)
+    u = pi_in(x, W_up, m_x)
+    g = pi_in(x, W_gate, m_x)
+    return {"u": u, "g": g, "s": u * ACTIVATIONS[act](g), "m_x": m_x}
+
+
 def channel_mask(s_tilde: np.ndarray, tau_s: float) -> np.ndarray:
     """[m_s]_j = 1[|s~_j| >= tau_s].  [blog] section "Stage 1", m_s equation."""
     return np.abs(np.asarray(s_tilde, dtype=np.float64)) >= np.float64(tau_s)
@@ -200,6 +218,17 @@ def decode(x, W_up, W_gate, W_down, q_up, sc_up, q_gate, sc_gate, tau_x, tau_s, 
             "s_sp": out["s"]}
 
 
+def decode_w16(x, W_up, W_gate, W_down, tau_x, tau_s, act="silu"):
+    """decode() with the 16-bit proxy (reading R20) in place of the INT4 one;
+    Stage 2 is unchanged."""
+    st = proxy_state_w16(x, W_up, W_gate, tau_x, act)
+    m_s = channel_mask(st["s"], tau_s)
+    out = stage2(x, W_up, W_gate, W_down, m_s, act)
+    return {"y": out["y"], "J": index_set(m_s), "k_x": int(st["m_x"].sum()),
+            "k_s": int(m_s.sum()), "s_tilde": st["s"], "m_x": st["m_x"], "m_s": m_s,
+            "s_sp": out["s"]}
+
+
 # --------------------------------------------------------------------------
 # C1-C2: offline calibration of the per-layer scalar thresholds
 # --------------------------------------------------------------------------
@@ -227,13 +256,25 @@ def calibrate(X_cal, q_up, sc_up, q_gate, sc_gate, keep_x: float, sparsity_s: fl
     s~ is the proxy state under tau_x (C2, reading R6).  keep fractions are
     evaluated as double(1) - double(sparsity) so both sides count alike.
     """
+    return calibrate_with(X_cal, lambda xt, tx: proxy_state(xt, q_up, sc_up, q_gate, sc_gate, tx, act)["s"],
+                          keep_x, sparsity_s)
+
+
+def calibrate_w16(X_cal, W_up, W_gate, keep_x: float, sparsity_s: float, act="silu"):
+    """calibrate() for the 16-bit proxy (reading R20): tau_s is taken over
+    the 16-bit proxy state."""
+    return calibrate_with(X_cal, lambda xt, tx: proxy_state_w16(xt, W_up, W_gate, tx, act)["s"],
+                          keep_x, sparsity_s)
+
+
+def calibrate_with(X_cal, state_fn, keep_x: float, sparsity_s: float):
+    """C1-C2 for a given proxy: state_fn(x_token, tau_x) returns the proxy
+    state s~ of one token under the fp32 input threshold tau_x."""
     X = np.asarray(X_cal, dtype=np.float64)
     ax = np.abs(X).ravel()
     tau_x = order_statistic_keep(ax, n_keep(float(keep_x), ax.size))
     tau_x32 = float(np.float32(tau_x)) if math.isfinite(tau_x) else math.inf
-    s_all = np.concatenate([
-        np.abs(proxy_state(X[t], q_up, sc_up, q_gate, sc_gate, tau_x32, act)["s"])
-        for t in range(X.shape[0])])
+    s_all = np.concatenate([np.abs(state_fn(X[t], tau_x32)) for t in range(X.shape[0])])
     keep_s = 1.0 - float(np.float32(sparsity_s))
     tau_s = order_statistic_keep(s_all, n_keep(keep_s, s_all.size))
     return tau_x32, tau_s

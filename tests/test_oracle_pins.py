@@ -417,3 +417,76 @@ def test_calibrate_hist_close_to_exact_calibration():
     exact_s = oracle.order_statistic_keep(pool.astype(np.float32), oracle.n_keep(1.0 - float(np.float32(0.7)), pool.size))
     ws_ = float(np.float32(np.float32(pool.astype(np.float32).max()) / np.float32(4096)))
     assert ts_h <= exact_s and exact_s - ts_h <= ws_ * (1 + 1e-6)
+
+
+# ---------------------------------------------------------------- 16-bit proxy (ablation A1, reading R20)
+def test_proxy_w16_equals_masked_dense_swiglu():
+    """The 16-bit proxy state is the SwiGLU intermediate of (x * m_x) against
+    the original weights (torch), for bf16 and fp32 layers."""
+    for dtype, seed in (("bf16", 41), ("f32", 42)):
+        layer = _small_layer(48, 80, dtype, seed=seed)
+        Wu, Wg, Wd, X, _ = _f64(layer)
+        for t in range(2):
+            x = X[t]
+            tau = float(np.float32(np.median(np.abs(x))))
+            st = oracle.proxy_state_w16(x, Wu, Wg, tau)
+            xm = np.where(np.abs(x) >= tau, x, 0.0)
+            _, s_ref = _torch_dense_swiglu(xm, Wu, Wg, Wd)
+            np.testing.assert_allclose(st["s"], s_ref, rtol=1e-12, atol=1e-15)
+            assert int(st["m_x"].sum()) == int(np.sum(np.abs(x) >= tau))
+
+
+def test_proxy_w16_bruteforce_loops():
+    """Tiny case written out as loops over the kept inputs."""
+    rng = np.random.default_rng(3)
+    d, f = 7, 5
+    Wu, Wg = rng.normal(size=(d, f)), rng.normal(size=(d, f))
+    x = rng.laplace(size=d)
+    tau = float(np.sort(np.abs(x))[3])
+    st = oracle.proxy_state_w16(x, Wu, Wg, tau)
+    for j in range(f):
+        u = sum(x[i] * Wu[i, j] for i in range(d) if abs(x[i]) >= tau)
+        g = sum(x[i] * Wg[i, j] for i in range(d) if abs(x[i]) >= tau)
+        assert math.isclose(st["s"][j], u * g / (1.0 + math.exp(-g)), rel_tol=1e-12, abs_tol=1e-15)
+
+
+def test_proxy_w16_with_dequantised_weights_is_the_int4_proxy():
+    """Fed the dequantised INT4 matrices, the 16-bit proxy path must give the
+    INT4 proxy state (both are Pi^in of the same matrices)."""
+    layer = _small_layer(40, 64, "bf16", seed=43)
+    Wu, Wg, _, X, _ = _f64(layer)
+    qu, su = oracle.pack_proxy(Wu)
+    qg, sg = oracle.pack_proxy(Wg)
+    tau = float(np.float32(np.median(np.abs(X[0]))))
+    a = oracle.proxy_state(X[0], qu, su, qg, sg, tau)
+    b = oracle.proxy_state_w16(X[0], oracle.dequantize(qu, su), oracle.dequantize(qg, sg), tau)
+    np.testing.assert_allclose(b["s"], a["s"], rtol=1e-12, atol=1e-15)
+
+
+def test_decode_w16_all_pass_and_empty():
+    layer = _small_layer(64, 96, "bf16", seed=44)
+    Wu, Wg, Wd, X, _ = _f64(layer)
+    out = oracle.decode_w16(X[0], Wu, Wg, Wd, 0.0, 0.0)
+    y_ref, _ = _torch_dense_swiglu(X[0], Wu, Wg, Wd)
+    assert out["k_s"] == Wu.shape[1] and out["k_x"] == Wu.shape[0]
+    assert np.linalg.norm(out["y"] - y_ref) / np.linalg.norm(y_ref) <= 1e-12
+    out = oracle.decode_w16(X[1], Wu, Wg, Wd, math.inf, 1e-6)
+    assert out["k_x"] == 0 and out["k_s"] == 0 and np.all(out["y"] == 0)
+
+
+def test_calibration_w16_bruteforce():
+    layer = _small_layer(32, 48, "bf16", seed=45)
+    Wu, Wg, _, _, Xc = _f64(layer)
+    tau_x, tau_s = oracle.calibrate_w16(Xc, Wu, Wg, 0.5, 0.7)
+    vals = sorted(abs(v) for v in Xc.ravel())
+    n = len(vals)
+    assert tau_x == float(np.float32(vals[n - math.ceil(0.5 * n)]))
+    svals = []
+    for t in range(Xc.shape[0]):
+        xm = np.where(np.abs(Xc[t]) >= tau_x, Xc[t], 0.0)
+        _, s = _torch_dense_swiglu(xm, Wu, Wg, np.zeros((Wu.shape[1], 1)))
+        svals.extend(abs(v) for v in s)
+    svals.sort()
+    ns = len(svals)
+    nks = math.ceil((1.0 - float(np.float32(0.7))) * ns)
+    assert math.isclose(tau_s, svals[ns - nks], rel_tol=1e-12)
