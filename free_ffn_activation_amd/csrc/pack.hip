@@ -200,6 +200,38 @@ hipError_t launch_pack(const void* w_up, const void* w_gate, int d, int f, int q
   return hipGetLastError();
 }
 
+// 16-bit proxy rows: row i = 16-column groups of {16 up, 16 gate} bf16 values
+// (64 bytes), then zero padding up to the row stride.  One thread per 16 bytes.
+__global__ __launch_bounds__(kThreads) void pack16_kernel(const uint16_t* wu, const uint16_t* wg, int d, int f,
+                                                          int stride, uint8_t* out) {
+  const size_t upr = static_cast<size_t>(stride) / 16;  // 16-byte units per row
+  const size_t n = static_cast<size_t>(d) * upr;
+  for (size_t idx = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; idx < n;
+       idx += static_cast<size_t>(gridDim.x) * kThreads) {
+    const size_t i = idx / upr;
+    const int u = static_cast<int>(idx - i * upr);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (u < f / 4) {
+      const int c = u >> 2;  // 16-column group
+      const int q = u & 3;   // 0, 1: up values 8q..; 2, 3: gate values 8(q-2)..
+      const uint16_t* src = (q < 2 ? wu : wg) + i * f + 16 * c + 8 * (q & 1);
+      v = *reinterpret_cast<const u32x4_t*>(src);
+    }
+    *reinterpret_cast<u32x4_t*>(out + i * stride + 16 * static_cast<size_t>(u)) = v;
+  }
+}
+
+hipError_t launch_pack16(const void* w_up, const void* w_gate, int d, int f, int stride, void* proxy_w16,
+                         hipStream_t s) {
+  const size_t n = static_cast<size_t>(d) * (stride / 16);
+  size_t blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(pack16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
+                     static_cast<const uint16_t*>(w_up), static_cast<const uint16_t*>(w_gate), d, f, stride,
+                     static_cast<uint8_t*>(proxy_w16));
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   if (bytes == 0) return hipSuccess;
   size_t blocks = (bytes / 4 + kThreads - 1) / kThreads;

@@ -57,10 +57,23 @@ prox_status check_layer(const prox_layer* L) {
   if (L->activation != PROX_ACT_SILU && L->activation != PROX_ACT_GELU_TANH)
     return fail(PROX_ERR_INVALID_ARG, "layer->activation %d is neither PROX_ACT_SILU nor PROX_ACT_GELU_TANH",
                 L->activation);
-  if (!L->proxy_q || !L->proxy_scale || !L->w_upgate_t || !L->w_down)
-    return fail(PROX_ERR_INVALID_ARG, "layer buffer pointer is NULL");
-  if (!aligned(L->proxy_q, 16) || !aligned(L->proxy_scale, 16) || !aligned(L->w_upgate_t, 16) ||
-      !aligned(L->w_down, 16))
+  if (L->reserved != 0) return fail(PROX_ERR_INVALID_ARG, "layer->reserved must be 0");
+  if (L->proxy_kind == PROX_PROXY_INT4) {
+    if (!L->proxy_q || !L->proxy_scale)
+      return fail(PROX_ERR_INVALID_ARG, "layer proxy_q / proxy_scale is NULL (PROX_PROXY_INT4)");
+    if (!aligned(L->proxy_q, 16) || !aligned(L->proxy_scale, 16))
+      return fail(PROX_ERR_INVALID_ARG, "layer buffers must be 16-byte aligned");
+  } else if (L->proxy_kind == PROX_PROXY_W16) {
+    if (L->wdtype != PROX_BF16)
+      return fail(PROX_ERR_UNSUPPORTED, "the 16-bit proxy is for bf16 layers (wdtype %d)", L->wdtype);
+    if (!L->proxy_w16) return fail(PROX_ERR_INVALID_ARG, "layer proxy_w16 is NULL (PROX_PROXY_W16)");
+    if (!aligned(L->proxy_w16, 16)) return fail(PROX_ERR_INVALID_ARG, "layer buffers must be 16-byte aligned");
+  } else {
+    return fail(PROX_ERR_INVALID_ARG, "layer->proxy_kind %d is neither PROX_PROXY_INT4 nor PROX_PROXY_W16",
+                L->proxy_kind);
+  }
+  if (!L->w_upgate_t || !L->w_down) return fail(PROX_ERR_INVALID_ARG, "layer buffer pointer is NULL");
+  if (!aligned(L->w_upgate_t, 16) || !aligned(L->w_down, 16))
     return fail(PROX_ERR_INVALID_ARG, "layer buffers must be 16-byte aligned");
   return PROX_OK;
 }
@@ -112,6 +125,9 @@ Stage1Args stage1_args(const Plan& p, const prox_layer* L, const void* x, float 
   a.in_count = in_count;
   a.act = L->activation;
   a.nt = 1;
+  a.proxy_kind = L->proxy_kind;
+  a.proxy16_stride = p.proxy16_stride;
+  a.proxy_w16 = L->proxy_w16;
   return a;
 }
 
@@ -226,7 +242,7 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
   // batch >= 2: groups of up to kBatchMax tokens read each proxy row and each
   // channel of the union once (Stage 2 on the matrix cores for bf16 weights)
   // unless PROX_STAGE_PER_TOKEN asks for the per-token kernels
-  const bool grouped = batch >= 2 && !(stages & PROX_STAGE_PER_TOKEN);
+  const bool grouped = batch >= 2 && !(stages & PROX_STAGE_PER_TOKEN) && layer->proxy_kind == PROX_PROXY_INT4;
   const bool grouped_s2 = grouped && layer->wdtype == PROX_BF16;
   const size_t es = elem_size(layer->wdtype);
   auto x_at = [&](int g0) { return static_cast<const uint8_t*>(x) + static_cast<size_t>(g0) * p.d * es; };
@@ -417,6 +433,7 @@ prox_status proxy_state_all(const Plan& p, const prox_layer* layer, const void* 
 
 // ---------------------------------------------------------------------------
 int proxy_row_stride(int f) { return ((f / 128) % 2 == 1) ? f : f + 128; }
+int proxy16_row_stride(int f) { return ((4 * f / 128) % 2 == 1) ? 4 * f : 4 * f + 128; }
 
 Plan make_plan(int d, int f, int wdtype) {
   Plan p;
@@ -424,6 +441,7 @@ Plan make_plan(int d, int f, int wdtype) {
   p.f = f;
   p.wdtype = wdtype;
   p.proxy_stride = proxy_row_stride(f);
+  p.proxy16_stride = proxy16_row_stride(f);
   // 128-column panels: wider panels gather faster but double the split
   // partials and the last block's reduction, which costs more than it saves
   p.panel = 128;
@@ -658,12 +676,49 @@ PROX_API prox_status prox_workspace_init(void* ws, size_t ws_bytes, void* stream
   }
 }
 
+PROX_API prox_status prox_proxy16_size(int32_t d, int32_t f, int32_t wdtype, size_t* bytes) {
+  try {
+    g_err.clear();
+    if (!bytes) return fail(PROX_ERR_INVALID_ARG, "bytes is NULL");
+    prox_status st = check_shape(d, f, wdtype);
+    if (st != PROX_OK) return st;
+    if (wdtype != PROX_BF16) return fail(PROX_ERR_UNSUPPORTED, "the 16-bit proxy is for bf16 layers");
+    *bytes = static_cast<size_t>(d) * proxy16_row_stride(f);
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_pack_proxy16(const void* W_up, const void* W_gate, const prox_layer* out, void* stream) {
+  try {
+    g_err.clear();
+    if (out == nullptr) return fail(PROX_ERR_INVALID_ARG, "layer descriptor is NULL");
+    prox_status st = check_shape(out->d_model, out->d_ff, out->wdtype);
+    if (st != PROX_OK) return st;
+    if (out->wdtype != PROX_BF16) return fail(PROX_ERR_UNSUPPORTED, "the 16-bit proxy is for bf16 layers");
+    if (!out->proxy_w16 || !aligned(out->proxy_w16, 16))
+      return fail(PROX_ERR_INVALID_ARG, "out->proxy_w16 must be non-NULL and 16-byte aligned");
+    if (!W_up || !W_gate) return fail(PROX_ERR_INVALID_ARG, "input weight pointer is NULL");
+    if (!aligned(W_up, 16) || !aligned(W_gate, 16))
+      return fail(PROX_ERR_INVALID_ARG, "input weights must be 16-byte aligned");
+    const hipError_t e = launch_pack16(W_up, W_gate, out->d_model, out->d_ff, proxy16_row_stride(out->d_ff),
+                                       out->proxy_w16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pack16 launch");
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 PROX_API prox_status prox_pack_proxy(const void* W_up, const void* W_gate, const void* W_down,
                                      const prox_layer* out, void* stream) {
   try {
     g_err.clear();
     prox_status st = check_layer(out);
     if (st != PROX_OK) return st;
+    if (!out->proxy_q || !out->proxy_scale)
+      return fail(PROX_ERR_INVALID_ARG, "out->proxy_q and out->proxy_scale receive the INT4 proxy: non-NULL");
     if (!W_up || !W_gate || !W_down) return fail(PROX_ERR_INVALID_ARG, "input weight pointer is NULL");
     if (!aligned(W_up, 16) || !aligned(W_gate, 16) || !aligned(W_down, 16))
       return fail(PROX_ERR_INVALID_ARG, "input weights must be 16-byte aligned");
@@ -823,7 +878,7 @@ PROX_API prox_status prox_proxy_state(const prox_layer* layer, const void* x, in
     if ((st = check_ws(p, batch, ws, ws_bytes)) != PROX_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (batch >= 2) {  // the grouped kernel, as prox_ffn_decode runs it
+    if (batch >= 2 && layer->proxy_kind == PROX_PROXY_INT4) {  // the grouped kernel, as prox_ffn_decode runs it
       const size_t es = elem_size(layer->wdtype);
       e = for_each_group(batch, [&](int g0, int nt) {
         Stage1Args a1 = stage1_args(p, layer, static_cast<const uint8_t*>(x) + static_cast<size_t>(g0) * p.d * es,

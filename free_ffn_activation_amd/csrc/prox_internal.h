@@ -26,6 +26,7 @@ struct Plan {
   int d, f, wdtype;
   // Stage 1
   int proxy_stride;  // bytes between proxy rows (odd multiple of 128)
+  int proxy16_stride;  // bytes between 16-bit proxy rows (odd multiple of 128)
   int panel;         // Stage-1 output columns per block (256 or 128)
   int n_panels;      // f / panel
   int splits;        // K-splits over input rows
@@ -63,6 +64,9 @@ struct Stage1Args {
   int* in_count;          // [batch] or nullptr
   int act;                // prox_activation
   int nt;                 // batched kernel: tokens in the group (2..8)
+  int proxy_kind;         // prox_proxy_kind
+  int proxy16_stride;     // PROX_PROXY_W16: bytes between proxy rows
+  const void* proxy_w16;  // PROX_PROXY_W16: [d][proxy16_stride] bf16 rows
 };
 
 // Batched Stage 2 (bf16 weights), one group of nt <= kBatchMax tokens; ws is
@@ -114,6 +118,10 @@ hipError_t launch_upgate(const UpGateArgs& a, int wdtype, int batch, int blocks,
                          bool from_bitmap, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, int wdtype, int batch, bool from_bitmap, hipStream_t s);
 hipError_t launch_stage1_batch(const Stage1Args& a, int wdtype, bool write_state, hipStream_t s);
+hipError_t launch_stage1_w16(const Stage1Args& a, int batch, bool write_state, hipStream_t s);
+int proxy16_row_stride(int f);
+hipError_t launch_pack16(const void* w_up, const void* w_gate, int d, int f, int stride, void* proxy_w16,
+                         hipStream_t s);
 hipError_t launch_upgate_batch(const UpGateBatchArgs& a, hipStream_t s);
 hipError_t launch_down_batch(const DownBatchArgs& a, float* y, hipStream_t s);
 size_t down_batch_smem(const DownBatchArgs& a);

@@ -289,6 +289,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
 
 hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_state,
                          hipStream_t s) {
+  if (a.proxy_kind == PROX_PROXY_W16) return launch_stage1_w16(a, batch, write_state, s);
   const dim3 grid(static_cast<unsigned>(a.n_panels * a.splits), static_cast<unsigned>(batch));
   const size_t kept_bytes =
       static_cast<size_t>(a.rows_per_split + 4) * (sizeof(KeptA) + sizeof(uint32_t));

@@ -25,6 +25,8 @@ PROX_F32 = 0
 PROX_BF16 = 1
 PROX_ACT_SILU = 0
 PROX_ACT_GELU_TANH = 1
+PROX_PROXY_INT4 = 0
+PROX_PROXY_W16 = 1  # the 16-bit proxy of the pages' precision ablation (bf16 layers)
 PROX_STAGE_PROXY = 1
 PROX_STAGE_UPGATE = 2
 PROX_STAGE_DOWN = 4
@@ -35,7 +37,7 @@ _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPO
 
 EXPORTED = ("prox_abi_version", "prox_last_error", "prox_layer_sizes", "prox_workspace_size",
             "prox_calibrate_workspace_size", "prox_budget_effective", "prox_budget_s2",
-            "prox_workspace_init", "prox_pack_proxy",
+            "prox_workspace_init", "prox_pack_proxy", "prox_proxy16_size", "prox_pack_proxy16",
             "prox_calibrate", "prox_calibrate_hist_workspace_size", "prox_calibrate_hist", "prox_ffn_decode", "prox_ffn_decode_events",
             "prox_ffn_decode_stages", "prox_ffn_stage2", "prox_proxy_state")
 
@@ -57,7 +59,7 @@ _c_i32, _c_f32, _c_size, _c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 class prox_layer(ctypes.Structure):
     _fields_ = [("d_model", _c_i32), ("d_ff", _c_i32), ("wdtype", _c_i32), ("activation", _c_i32),
                 ("proxy_q", _c_vp), ("proxy_scale", _c_vp), ("w_upgate_t", _c_vp),
-                ("w_down", _c_vp)]
+                ("w_down", _c_vp), ("proxy_kind", _c_i32), ("reserved", _c_i32), ("proxy_w16", _c_vp)]
 
 
 _P = ctypes.POINTER
@@ -74,6 +76,8 @@ _sig = {
     "prox_calibrate_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
     "prox_workspace_init": (_c_i32, [_c_vp, _c_size, _c_vp]),
     "prox_pack_proxy": (_c_i32, [_c_vp, _c_vp, _c_vp, _P(prox_layer), _c_vp]),
+    "prox_proxy16_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
+    "prox_pack_proxy16": (_c_i32, [_c_vp, _c_vp, _P(prox_layer), _c_vp]),
     "prox_calibrate": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _P(_c_f32),
                                 _P(_c_f32), _c_vp, _c_size, _c_vp]),
     "prox_ffn_decode": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_vp, _c_vp,
@@ -172,18 +176,27 @@ class ProxLayer:
     """Device buffers of one packed layer (allocated by torch) and their
     prox_layer descriptor."""
 
-    def __init__(self, d_model: int, d_ff: int, wdtype: int, device="cuda", activation: int = 0):
+    def __init__(self, d_model: int, d_ff: int, wdtype: int, device="cuda", activation: int = 0,
+                 proxy16: bool = False):
+        """proxy16 also allocates the 16-bit proxy buffer (proxy_w16, bf16 layers);
+        the descriptor still selects the INT4 proxy until with_proxy_kind()."""
         sizes = prox_layer_sizes(d_model, d_ff, wdtype)
         self.d_model, self.d_ff, self.wdtype, self.activation = d_model, d_ff, wdtype, activation
+        self.proxy_kind = PROX_PROXY_INT4
         wt = torch.float32 if wdtype == PROX_F32 else torch.int16
         es = 4 if wdtype == PROX_F32 else 2
         self.proxy_q = torch.empty(sizes[0], dtype=torch.uint8, device=device)
         self.proxy_scale = torch.empty(sizes[1] // 4, dtype=torch.float32, device=device)
         self.w_upgate_t = torch.empty(sizes[2] // es, dtype=wt, device=device)
         self.w_down = torch.empty(sizes[3] // es, dtype=wt, device=device)
-        self.desc = prox_layer(d_model, d_ff, wdtype, activation, self.proxy_q.data_ptr(),
-                               self.proxy_scale.data_ptr(), self.w_upgate_t.data_ptr(),
-                               self.w_down.data_ptr())
+        self.proxy_w16 = (torch.zeros(prox_proxy16_size(d_model, d_ff, wdtype), dtype=torch.uint8, device=device)
+                          if proxy16 else None)
+        self.desc = self._make_desc()
+
+    def _make_desc(self) -> prox_layer:
+        return prox_layer(self.d_model, self.d_ff, self.wdtype, self.activation, self.proxy_q.data_ptr(),
+                          self.proxy_scale.data_ptr(), self.w_upgate_t.data_ptr(), self.w_down.data_ptr(),
+                          self.proxy_kind, 0, self.proxy_w16.data_ptr() if self.proxy_w16 is not None else None)
 
     def with_activation(self, activation: int) -> "ProxLayer":
         """Another descriptor over the same packed buffers with a different gate
@@ -191,15 +204,26 @@ class ProxLayer:
         other = object.__new__(ProxLayer)
         other.__dict__.update(self.__dict__)
         other.activation = activation
-        other.desc = prox_layer(self.d_model, self.d_ff, self.wdtype, activation, self.proxy_q.data_ptr(),
-                                self.proxy_scale.data_ptr(), self.w_upgate_t.data_ptr(),
-                                self.w_down.data_ptr())
+        other.desc = other._make_desc()
+        return other
+
+    def with_proxy_kind(self, kind: int) -> "ProxLayer":
+        """Another descriptor over the same buffers whose Stage 1 reads the given
+        proxy (PROX_PROXY_INT4 or PROX_PROXY_W16)."""
+        if kind == PROX_PROXY_W16 and self.proxy_w16 is None:
+            raise ValueError("this layer has no 16-bit proxy buffer (ProxLayer(..., proxy16=True))")
+        other = object.__new__(ProxLayer)
+        other.__dict__.update(self.__dict__)
+        other.proxy_kind = kind
+        other.desc = other._make_desc()
         return other
 
     @property
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size()
-                   for t in (self.proxy_q, self.proxy_scale, self.w_upgate_t, self.w_down))
+        bufs = [self.proxy_q, self.proxy_scale, self.w_upgate_t, self.w_down]
+        if self.proxy_w16 is not None:
+            bufs.append(self.proxy_w16)
+        return sum(t.numel() * t.element_size() for t in bufs)
 
 
 def new_workspace(d_model: int, d_ff: int, batch: int, device="cuda") -> torch.Tensor:
@@ -221,6 +245,22 @@ def prox_pack_proxy(W_up: torch.Tensor, W_gate: torch.Tensor, W_down: torch.Tens
             raise ValueError(f"weight of shape {tuple(t.shape)} / {t.dtype}, expected {shape}")
     _check(_lib.prox_pack_proxy(_ptr(W_up), _ptr(W_gate), _ptr(W_down), ctypes.byref(layer.desc),
                                 _stream(stream)))
+
+
+def prox_proxy16_size(d_model: int, d_ff: int, wdtype: int) -> int:
+    out = _c_size()
+    _check(_lib.prox_proxy16_size(d_model, d_ff, wdtype, ctypes.byref(out)))
+    return int(out.value)
+
+
+def prox_pack_proxy16(W_up: torch.Tensor, W_gate: torch.Tensor, layer: ProxLayer, stream=None) -> None:
+    d, f = layer.d_model, layer.d_ff
+    for t in (W_up, W_gate):
+        if tuple(t.shape) != (d, f) or _wdtype_of(t) != layer.wdtype:
+            raise ValueError(f"weight of shape {tuple(t.shape)} / {t.dtype}, expected {(d, f)}")
+    if layer.proxy_w16 is None:
+        raise ValueError("layer has no 16-bit proxy buffer (ProxLayer(..., proxy16=True))")
+    _check(_lib.prox_pack_proxy16(_ptr(W_up), _ptr(W_gate), ctypes.byref(layer.desc), _stream(stream)))
 
 
 def prox_calibrate(layer: ProxLayer, X_cal: torch.Tensor, keep_x: float, sparsity_s: float,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PROX_ABI_VERSION 2
+#define PROX_ABI_VERSION 3
 
 typedef enum {
   PROX_OK = 0,
@@ -87,8 +87,23 @@ typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
  *             0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))).  The pages
  *             evaluate the method on SwiGLU models and on GeGLU-style Gemma-3
  *             ([blog] evidence section).
+ * proxy_kind  which proxy Stage 1 reads: PROX_PROXY_INT4 (proxy_q and
+ *             proxy_scale, the method's proxy) or PROX_PROXY_W16, the 16-bit
+ *             proxy of the pages' precision ablation ([blog] evidence section,
+ *             ablation A1: a 16-bit proxy in place of INT4 at the same budget),
+ *             here the layer's own bf16 weights (bf16 layers only).  Stage 2
+ *             is the same for both.  A grouped batch (batch >= 2) runs the
+ *             grouped kernels for INT4 and the per-token kernels for W16.
+ * reserved    must be 0.
+ * proxy_w16   PROX_PROXY_W16 only (may be NULL otherwise): [d_model][wstride]
+ *             bytes, wstride = 4 d_ff rounded to an odd multiple of 128 (zero
+ *             padding).  Row i holds W_up[i, :] and W_gate[i, :] as bf16 in the
+ *             column groups of proxy_q: each group of 16 output columns takes
+ *             64 bytes, the 16 up values then the 16 gate values.
+ * With PROX_PROXY_W16, proxy_q and proxy_scale may be NULL.
  */
 typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
+typedef enum { PROX_PROXY_INT4 = 0, PROX_PROXY_W16 = 1 } prox_proxy_kind;
 
 typedef struct {
   int32_t d_model;
@@ -99,6 +114,9 @@ typedef struct {
   float* proxy_scale;
   void* w_upgate_t;
   void* w_down;
+  int32_t proxy_kind; /* prox_proxy_kind */
+  int32_t reserved;
+  void* proxy_w16;
 } prox_layer;
 
 /* Version of this ABI (PROX_ABI_VERSION). */
@@ -160,6 +178,21 @@ prox_status prox_workspace_init(void* ws, size_t ws_bytes, void* stream);
  */
 prox_status prox_pack_proxy(const void* W_up, const void* W_gate, const void* W_down,
                             const prox_layer* out, void* stream);
+
+/*
+ * Bytes of the 16-bit proxy (proxy_w16) of a bf16 layer: d_model * wstride.
+ * f32 layers give PROX_ERR_UNSUPPORTED.
+ */
+prox_status prox_proxy16_size(int32_t d_model, int32_t d_ff, int32_t wdtype, size_t* bytes);
+
+/*
+ * Offline packing of the 16-bit proxy ([blog] evidence section, ablation A1):
+ * copies W_up and W_gate (device [d_model][d_ff] bf16, paper orientation)
+ * into out->proxy_w16 in the layout documented at prox_layer, padding zeroed.
+ * bf16 layers only (PROX_ERR_UNSUPPORTED otherwise); out->proxy_w16 must be
+ * non-NULL and 16-byte aligned.  Asynchronous.
+ */
+prox_status prox_pack_proxy16(const void* W_up, const void* W_gate, const prox_layer* out, void* stream);
 
 /*
  * Offline calibration of the two per-layer scalar thresholds ([blog] evidence

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_sizes():
-    assert P.prox_abi_version() == 2
+    assert P.prox_abi_version() == 3
     s = P.prox_layer_sizes(4096, 12288, P.PROX_BF16)
     assert s == (4096 * (12288 + 128), 2 * 4096 * 4, 2 * 12288 * 4096 * 2, 12288 * 4096 * 2)
     assert P.prox_layer_sizes(128, 384, P.PROX_BF16)[0] == 128 * 384     # 384/128 odd: no padding
@@ -63,7 +63,7 @@ FAKE = 1 << 40  # a 256-aligned address that is never dereferenced by validation
 
 
 def _layer(d=256, f=768, dt=0, **kw):
-    L = P.prox_layer(d, f, dt, 0, FAKE, FAKE, FAKE, FAKE)
+    L = P.prox_layer(d, f, dt, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, None)
     for k, v in kw.items():
         setattr(L, k, v)
     return L
@@ -81,6 +81,13 @@ def test_decode_argument_validation():
     assert _decode(None) == P.PROX_ERR_INVALID_ARG
     assert _decode(_layer(proxy_q=None)) == P.PROX_ERR_INVALID_ARG
     assert _decode(_layer(activation=2)) == P.PROX_ERR_INVALID_ARG
+    # proxy kind: unknown kinds, a non-zero reserved field, the 16-bit proxy
+    # without its buffer or on an fp32 layer are rejected before any work
+    assert _decode(_layer(proxy_kind=2)) == P.PROX_ERR_INVALID_ARG
+    assert _decode(_layer(reserved=1)) == P.PROX_ERR_INVALID_ARG
+    assert _decode(_layer(dt=P.PROX_BF16, proxy_kind=P.PROX_PROXY_W16)) == P.PROX_ERR_INVALID_ARG
+    assert _decode(_layer(proxy_kind=P.PROX_PROXY_W16, proxy_w16=FAKE)) == P.PROX_ERR_UNSUPPORTED
+    assert _decode(_layer(dt=P.PROX_BF16, proxy_kind=P.PROX_PROXY_W16, proxy_w16=FAKE + 8)) == P.PROX_ERR_INVALID_ARG
     assert _decode(_layer(d=250)) == P.PROX_ERR_UNSUPPORTED
     assert _decode(_layer(w_down=FAKE + 8)) == P.PROX_ERR_INVALID_ARG     # misaligned
     assert _decode(ok_layer, batch=0) == P.PROX_ERR_INVALID_ARG
@@ -137,3 +144,23 @@ def test_other_entry_points_validate():
     for bad in (0, 8, 16, 24, -1):
         assert lib.prox_ffn_decode_stages(ctypes.byref(L), FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE,
                                           None, FAKE, 1 << 30, None, bad) == P.PROX_ERR_INVALID_ARG
+
+
+def test_proxy16_sizes_and_pack_validation():
+    # rows of 4 * d_ff bytes, padded to an odd multiple of 128 (d_ff % 128 == 0
+    # makes 4 * d_ff / 128 even, so every row carries 128 bytes of padding)
+    assert P.prox_proxy16_size(4096, 12288, P.PROX_BF16) == 4096 * (4 * 12288 + 128)
+    assert P.prox_proxy16_size(64, 128, P.PROX_BF16) == 64 * (512 + 128)
+    assert P.prox_proxy16_size(128, 384, P.PROX_BF16) == 128 * (1536 + 128)
+    with pytest.raises(P.ProxError) as ei:
+        P.prox_proxy16_size(256, 768, P.PROX_F32)
+    assert ei.value.status == P.PROX_ERR_UNSUPPORTED
+    # argument checks happen before anything is enqueued (no GPU work here)
+    lib = P.raw_library()
+    assert lib.prox_pack_proxy16(None, FAKE, ctypes.byref(_layer(dt=P.PROX_BF16, proxy_w16=FAKE)), None) == \
+        P.PROX_ERR_INVALID_ARG
+    assert lib.prox_pack_proxy16(FAKE, FAKE, None, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_pack_proxy16(FAKE, FAKE, ctypes.byref(_layer(dt=P.PROX_BF16)), None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_pack_proxy16(FAKE, FAKE, ctypes.byref(_layer(proxy_w16=FAKE)), None) == P.PROX_ERR_UNSUPPORTED
+    assert lib.prox_pack_proxy16(FAKE + 8, FAKE, ctypes.byref(_layer(dt=P.PROX_BF16, proxy_w16=FAKE)), None) == \
+        P.PROX_ERR_INVALID_ARG
