@@ -541,6 +541,86 @@ def main() -> int:
                        "seconds": round(time.perf_counter() - t_cal0, 2)}
         del hws, cws, hdws
 
+    # ---------------------------------------------------------------- 16-bit proxy (ablation A1)
+    # The pages' precision ablation swaps the INT4 proxy for a 16-bit one at the
+    # same budget.  Here the 16-bit proxy is each rotated layer's own bf16
+    # W_up / W_gate (built on the GPU from the packed transposed weights):
+    # its Stage 1 over every input gives alpha_16, the allocator turns the same
+    # effective-sparsity targets at s1 = 0.7 into s2 (or reports them out of
+    # reach), and the reachable points and the headline configuration are timed.
+    proxy16 = None
+    if not args.no_budget and cfg.dtype == "bf16":
+        for L in layers:
+            L.add_proxy16()
+            wt = L.w_upgate_t.view(f, 2, d)
+            prox.prox_pack_proxy16(wt[:, 0, :].t().contiguous(), wt[:, 1, :].t().contiguous(), L)
+        torch.cuda.synchronize()
+        layers16 = [L.with_proxy_kind(prox.PROX_PROXY_W16) for L in layers]
+        py16 = torch.empty(1, d, dtype=torch.float32, device=dev)
+        pmi16 = torch.empty(1, f, dtype=torch.int32, device=dev)
+        pmc16 = torch.empty(1, dtype=torch.int32, device=dev)
+        pic16 = torch.empty(1, dtype=torch.int32, device=dev)
+        pws16 = prox.new_workspace(d, f, 1)
+
+        def s1_16(tx_of):
+            def fn(s):
+                l, t = sched[s % steps_per_round]
+                prox.prox_ffn_decode_stages(layers16[l], xs[l][t], tx_of(l), taus[l][1], py16, pmi16, pmc16, pic16,
+                                            pws16, prox.PROX_STAGE_PROXY)
+            return fn
+
+        t16_all = time_graph(s1_16(lambda l: 0.0), "16-bit proxy: Stage 1 over every input")[0]
+        alpha16 = t16_all / t_proj
+        taus16 = [prox.prox_calibrate(layers16[l], x_cal[l], cfg.keep_x, sparsity, cal_ws) for l in range(n_layers)]
+        t16_s1 = time_graph(s1_16(lambda l: taus16[l][0]), "16-bit proxy: Stage 1 alone (keep_x 0.5)")[0]
+
+        def dec16(tl):
+            def fn(s):
+                l, t = sched[s % steps_per_round]
+                prox.prox_ffn_decode(layers16[l], xs[l][t], tl[l][0], tl[l][1], py16, pmi16, pmc16, pic16, pws16)
+            return fn
+
+        def counts16(tl):
+            kx_a = np.zeros((n_layers, n_tok), np.int64)
+            ks_a = np.zeros((n_layers, n_tok), np.int64)
+            for l in range(n_layers):
+                for t in range(n_tok):
+                    prox.prox_ffn_decode(layers16[l], xs[l][t], tl[l][0], tl[l][1], py16, pmi16, pmc16, pic16, pws16)
+                    torch.cuda.synchronize()
+                    kx_a[l, t], ks_a[l, t] = int(pic16.item()), int(pmc16.item())
+            return kx_a, ks_a
+
+        us16 = time_graph(dec16(taus16), "16-bit proxy decode (keep_x 0.5, s2 0.7)")[0]
+        kx16, ks16 = counts16(taus16)
+        mb16 = sched_mean(4 * kx16 * f + 3 * ks16 * d * w + d * w + 4 * d + 4 * ks16)
+        pts16 = []
+        for e_t in (0.4, 0.5, 0.6, 0.7):
+            try:
+                s2p = prox.prox_budget_s2(e_t, 0.7, alpha16)
+            except prox.ProxError as exc:
+                if exc.status != prox.PROX_ERR_UNSUPPORTED:
+                    raise
+                pts16.append({"e_target": e_t, "s1": 0.7, "reachable": False, "reason": str(exc)})
+                continue
+            tl = [prox.prox_calibrate(layers16[l], x_cal[l], 0.3, s2p, cal_ws) for l in range(n_layers)]
+            us_p = time_graph(dec16(tl), f"16-bit proxy decode at e={e_t} s1=0.7 s2={s2p:.4f}")[0]
+            kx_p, ks_p = counts16(tl)
+            pts16.append({"e_target": e_t, "s1": 0.7, "s2": round(s2p, 4), "reachable": True,
+                          "us_per_layer": round(us_p, 3), "runtime_keep_s": round(sched_mean(ks_p) / f, 4)})
+        proxy16 = {"proxy": "the layer's own bf16 W_up / W_gate, row-major", "alpha": round(alpha16, 4),
+                   "alpha_int4": round(alpha, 4), "t_stage1_all_inputs_us": round(t16_all, 3),
+                   "t_stage1_us": round(t16_s1, 3), "t_stage1_int4_us": round(float(k_mean[0]), 3),
+                   "us_per_layer": round(us16, 3), "required_MB": round(mb16 / 1e6, 3),
+                   "mean_k_x": round(sched_mean(kx16), 1), "mean_k_s": round(sched_mean(ks16), 1),
+                   "same_budget_s1_0.7": pts16,
+                   "proxy_bytes_per_layer": int(layers[0].proxy_w16.numel())}
+        log(f"16-bit proxy: alpha {alpha16:.3f} (INT4 {alpha:.3f}); Stage 1 {t16_s1:.2f} us (INT4 {k_mean[0]:.2f}); "
+            f"decode {us16:.2f} us at keep_x 0.5 / s2 0.7")
+        for L in layers:
+            L.proxy_w16 = None
+            L.desc = L._make_desc()
+        del layers16, pws16
+
     # ---------------------------------------------------------------- GeGLU layers
     # the same packed layers read as GeGLU (GELU-tanh gate), recalibrated at the
     # headline keep / sparsity, timed over the same rotation
@@ -754,6 +834,7 @@ def main() -> int:
         "geglu": geglu,
         "calibration": calibration,
         "batch8": batch8,
+        "proxy16": proxy16,
     }
     print(json.dumps(out), flush=True)
     return 0

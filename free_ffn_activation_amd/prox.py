@@ -207,6 +207,14 @@ class ProxLayer:
         other.desc = other._make_desc()
         return other
 
+    def add_proxy16(self, device="cuda") -> None:
+        """Allocate the 16-bit proxy buffer of an existing layer (fill it with
+        prox_pack_proxy16, select it with with_proxy_kind)."""
+        if self.proxy_w16 is None:
+            self.proxy_w16 = torch.zeros(prox_proxy16_size(self.d_model, self.d_ff, self.wdtype),
+                                         dtype=torch.uint8, device=device)
+            self.desc = self._make_desc()
+
     def with_proxy_kind(self, kind: int) -> "ProxLayer":
         """Another descriptor over the same buffers whose Stage 1 reads the given
         proxy (PROX_PROXY_INT4 or PROX_PROXY_W16)."""
