@@ -237,58 +237,79 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
     for (int i = 0; i < 4; ++i)
       if (!events[i]) return fail(PROX_ERR_INVALID_ARG, "events[%d] is NULL", i);
   }
-  if ((stages & 7) == 0 || stages < 0 || stages > 15)
-    return fail(PROX_ERR_INVALID_ARG, "stages %d is not a non-empty subset of 1|2|4 (plus 8)", stages);
-  // batch >= 2: groups of up to kBatchMax tokens read each proxy row and each
-  // channel of the union once (Stage 2 on the matrix cores for bf16 weights)
-  // unless PROX_STAGE_PER_TOKEN asks for the per-token kernels
-  const bool grouped = batch >= 2 && !(stages & PROX_STAGE_PER_TOKEN) && layer->proxy_kind == PROX_PROXY_INT4;
-  const bool grouped_s2 = grouped && layer->wdtype == PROX_BF16;
+  if ((stages & 7) == 0 || stages < 0 || stages > 31 ||
+      ((stages & PROX_STAGE_PER_TOKEN) && (stages & PROX_STAGE_GROUPED)))
+    return fail(PROX_ERR_INVALID_ARG, "stages %d: a non-empty subset of 1|2|4, plus at most one of 8 and 16",
+                stages);
+  // Kernels per group of nt <= kBatchMax tokens: the grouped ones (each proxy
+  // row and channel of the group's unions read once; Stage 2 grouped for bf16
+  // weights, INT4 proxy only) from kGroupedMinTokens tokens up, where they are
+  // faster, the per-token ones below; PROX_STAGE_PER_TOKEN / PROX_STAGE_GROUPED
+  // force either for every group.
+  auto grouped1 = [&](int nt) {
+    if (batch < 2 || layer->proxy_kind != PROX_PROXY_INT4 || (stages & PROX_STAGE_PER_TOKEN)) return false;
+    return (stages & PROX_STAGE_GROUPED) != 0 || nt >= kGroupedMinTokens;
+  };
+  auto grouped2 = [&](int nt) { return grouped1(nt) && layer->wdtype == PROX_BF16; };
+  bool any1 = false, any2 = false;
+  for (int g0 = 0; g0 < batch; g0 += kBatchMax) {
+    const int nt = std::min<int>(kBatchMax, batch - g0);
+    any1 = any1 || grouped1(nt);
+    any2 = any2 || grouped2(nt);
+  }
   const size_t es = elem_size(layer->wdtype);
   auto x_at = [&](int g0) { return static_cast<const uint8_t*>(x) + static_cast<size_t>(g0) * p.d * es; };
   auto ws_at = [&](int g0) { return static_cast<uint8_t*>(ws) + static_cast<size_t>(g0) * p.tok_bytes; };
+  auto mi_at = [&](int g0) { return mask_idx + static_cast<size_t>(g0) * p.f; };
+  auto y_at = [&](int g0) { return y + static_cast<size_t>(g0) * p.d; };
+  auto ic_at = [&](int g0) { return in_count ? in_count + g0 : nullptr; };
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   if (stages & PROX_STAGE_PROXY) {
-    if (grouped) {
+    if (!any1) {
+      e = launch_stage1(stage1_args(p, layer, x, tau_x, tau_s, ws, nullptr, in_count), layer->wdtype, batch,
+                        false, s);
+    } else {
       e = for_each_group(batch, [&](int g0, int nt) {
-        Stage1Args a1 = stage1_args(p, layer, x_at(g0), tau_x, tau_s, ws_at(g0), nullptr,
-                                    in_count ? in_count + g0 : nullptr);
+        Stage1Args a1 = stage1_args(p, layer, x_at(g0), tau_x, tau_s, ws_at(g0), nullptr, ic_at(g0));
+        if (!grouped1(nt)) return launch_stage1(a1, layer->wdtype, nt, false, s);
         a1.nt = nt;
         return launch_stage1_batch(a1, layer->wdtype, false, s);
       });
-    } else {
-      e = launch_stage1(stage1_args(p, layer, x, tau_x, tau_s, ws, nullptr, in_count), layer->wdtype,
-                        batch, false, s);
     }
     if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
   }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   if (stages & PROX_STAGE_UPGATE) {
-    if (grouped_s2) {
-      e = for_each_group(batch, [&](int g0, int nt) {
-        return launch_upgate_batch(upgate_batch_args(p, layer, x_at(g0), ws_at(g0), nt,
-                                                     mask_idx + static_cast<size_t>(g0) * p.f, mask_count + g0),
-                                   s);
-      });
-    } else {
+    if (!any2) {
       e = launch_upgate(upgate_args(p, layer, x, ws, mask_idx, mask_count, y), layer->wdtype, batch,
                         p.ug_blocks, true, s);
+    } else {
+      e = for_each_group(batch, [&](int g0, int nt) {
+        if (!grouped2(nt))
+          return launch_upgate(upgate_args(p, layer, x_at(g0), ws_at(g0), mi_at(g0), mask_count + g0, y_at(g0)),
+                               layer->wdtype, nt, p.ug_blocks, true, s);
+        return launch_upgate_batch(upgate_batch_args(p, layer, x_at(g0), ws_at(g0), nt, mi_at(g0), mask_count + g0),
+                                   s);
+      });
     }
     if (e != hipSuccess) return hip_fail(e, "stage-2 up/gate launch");
   }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[2]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   if (stages & PROX_STAGE_DOWN) {
-    if (grouped_s2) {
-      e = for_each_group(batch, [&](int g0, int nt) {
-        return launch_down_batch(down_batch_args(p, layer, ws_at(g0), nt), y + static_cast<size_t>(g0) * p.d, s);
-      });
-    } else {
+    if (!any2) {
       e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, true, s);
+    } else {
+      e = for_each_group(batch, [&](int g0, int nt) {
+        if (!grouped2(nt))
+          return launch_down(down_args(p, layer, ws_at(g0), mi_at(g0), mask_count + g0, y_at(g0)), layer->wdtype, nt,
+                             true, s);
+        return launch_down_batch(down_batch_args(p, layer, ws_at(g0), nt), y_at(g0), s);
+      });
     }
     if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
   }
@@ -878,12 +899,13 @@ PROX_API prox_status prox_proxy_state(const prox_layer* layer, const void* x, in
     if ((st = check_ws(p, batch, ws, ws_bytes)) != PROX_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (batch >= 2 && layer->proxy_kind == PROX_PROXY_INT4) {  // the grouped kernel, as prox_ffn_decode runs it
+    if (batch >= 2 && layer->proxy_kind == PROX_PROXY_INT4) {  // per group, as prox_ffn_decode runs it
       const size_t es = elem_size(layer->wdtype);
       e = for_each_group(batch, [&](int g0, int nt) {
         Stage1Args a1 = stage1_args(p, layer, static_cast<const uint8_t*>(x) + static_cast<size_t>(g0) * p.d * es,
                                     tau_x, INFINITY, static_cast<uint8_t*>(ws) + static_cast<size_t>(g0) * p.tok_bytes,
                                     s_tilde + static_cast<size_t>(g0) * p.f, in_count ? in_count + g0 : nullptr);
+        if (nt < kGroupedMinTokens) return launch_stage1(a1, layer->wdtype, nt, true, s);
         a1.nt = nt;
         return launch_stage1_batch(a1, layer->wdtype, true, s);
       });

@@ -18,6 +18,7 @@ constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
 constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column slice
 constexpr int kBatchMax = 8;           // tokens per group of the batched kernels
+constexpr int kGroupedMinTokens = 4;   // smaller groups run the per-token kernels (faster there)
 
 // ---------------------------------------------------------------------------
 // Per-launch plan (host-computed, passed by value to kernels)

@@ -248,7 +248,9 @@ prox_status prox_calibrate_hist(const prox_layer* layer, const void* X_cal, int3
  *   in_count    device [batch] int32 (k_x per token) or NULL
  *   ws          device, >= prox_workspace_size(batch) bytes, zeroed once
  * Asynchronous: kernels on `stream`, no host synchronisation.  batch 1 runs
- * three kernels.  batch >= 2 runs groups of up to 8 tokens (the pages study
+ * three kernels.  batch >= 2 runs groups of up to 8 tokens; a group of 4 or
+ * more tokens runs the grouped kernels, a smaller one the per-token kernels
+ * (prox_ffn_decode_stages can force either).  Grouped (the pages study
  * batch 1 and leave larger batches open, [blog] limitations section): Stage 1
  * reads each proxy row of the union of the group's kept input rows once and
  * gives a token a zero weight on the rows it rejects; for bf16 weights Stage 2
@@ -289,9 +291,12 @@ prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32
 #define PROX_STAGE_UPGATE 2
 #define PROX_STAGE_DOWN 4
 /* with batch >= 2: run the per-token kernels (each token reads its own rows
- * and channels) instead of the grouped ones; same results up to fp32
- * summation order */
+ * and channels) for every group; same results up to fp32 summation order */
 #define PROX_STAGE_PER_TOKEN 8
+/* with batch >= 2: run the grouped kernels for every group (by default a group
+ * of fewer than 4 tokens runs the per-token kernels, which are faster there);
+ * not together with PROX_STAGE_PER_TOKEN */
+#define PROX_STAGE_GROUPED 16
 prox_status prox_ffn_decode_stages(const prox_layer* layer, const void* x, int32_t batch,
                                    float tau_x, float tau_s, float* y, int32_t* mask_idx,
                                    int32_t* mask_count, int32_t* in_count, void* ws,
@@ -311,8 +316,8 @@ prox_status prox_ffn_stage2(const prox_layer* layer, const void* x, int32_t batc
 
 /*
  * Stage 1 alone: the proxy state s~ ([blog] "Stage 1", equations for u~, h~,
- * s~) for every channel.  batch >= 2 runs the grouped Stage-1 kernel, as
- * prox_ffn_decode does, so s~ is what the decode thresholds.
+ * s~) for every channel.  Groups of tokens run the Stage-1 kernel that
+ * prox_ffn_decode runs for them, so s~ is what the decode thresholds.
  *   s_tilde     device [batch][d_ff] fp32
  *   in_count    device [batch] int32 or NULL
  * Asynchronous.

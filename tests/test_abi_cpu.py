@@ -140,8 +140,9 @@ def test_other_entry_points_validate():
                                    ctypes.byref(ts), FAKE, 16, None) == P.PROX_ERR_INVALID_ARG
     assert lib.prox_calibrate_hist(ctypes.byref(L), FAKE, 64, 0.5, 1.5, 200000, 4096, ctypes.byref(tx),
                                    ctypes.byref(ts), FAKE, 1 << 30, None) == P.PROX_ERR_INVALID_ARG
-    # stage subsets must be a non-empty subset of the three kernels
-    for bad in (0, 8, 16, 24, -1):
+    # stage subsets: a non-empty subset of the three kernels, plus at most one
+    # of the per-token / grouped overrides
+    for bad in (0, 8, 16, 24, -1, 32, 7 | 8 | 16, 1 | 8 | 16, 39):
         assert lib.prox_ffn_decode_stages(ctypes.byref(L), FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE,
                                           None, FAKE, 1 << 30, None, bad) == P.PROX_ERR_INVALID_ARG
 

@@ -1,6 +1,8 @@
 """GPU parity of the grouped batch path (2..8 tokens per group, more tokens in
 several groups): Stage 1 over the union of the group's kept rows on the matrix
-cores, Stage 2 over the union of the channel lists (bf16 weights).
+cores, Stage 2 over the union of the channel lists (bf16 weights).  By default
+groups of fewer than 4 tokens run the per-token kernels; PROX_STAGE_GROUPED
+forces the grouped ones so that small groups are covered too.
 
 Every token is checked against the CPU oracle run on that token alone (the
 batch-1 definition): k_x exact, channel masks exact outside the 1e-3 tau_s
@@ -96,6 +98,13 @@ def test_grouped_decode_parity(P, d, f, dtype, batch, seed):
     ws = P.new_workspace(d, f, batch)
     out = _decode(P, L, x, tau_x, tau_s, ws)
     _check_tokens(ov, ov["x_dec"], out, tau_x, tau_s, f"{d}x{f}-{dtype}-b{batch}")
+    forced = _decode(P, L, x, tau_x, tau_s, ws, stages=7 | P.PROX_STAGE_GROUPED)
+    _check_tokens(ov, ov["x_dec"], forced, tau_x, tau_s, f"{d}x{f}-{dtype}-b{batch}-grouped")
+    if batch < 4:  # the default ran the per-token kernels: same lists as forcing them
+        pt = _decode(P, L, x, tau_x, tau_s, ws, stages=7 | P.PROX_STAGE_PER_TOKEN)
+        assert all(np.array_equal(a, b) for a, b in zip(out[1:], pt[1:]))
+        # y: the per-token down kernel sums with atomics, so only up to fp32 order
+        assert y_errors(out[0], pt[0].astype(np.float64))[1] <= 1e-5
 
 
 def test_grouped_qwen3_8b_batch8_and_per_token_kernels(P):
@@ -194,12 +203,15 @@ def test_grouped_repeat_graph_and_workspace_reuse(P):
     x3 = to_device(layer.x_dec[2:5], "bf16")
     ws = P.new_workspace(L.d_model, L.d_ff, 8)
     ref8 = _decode(P, L, x8, tau_x, tau_s, ws)
-    ref3 = _decode(P, L, x3, tau_x, tau_s, ws)
+    G = 7 | P.PROX_STAGE_GROUPED  # three tokens: grouped kernels forced (bit-reproducible y)
+    ref3 = _decode(P, L, x3, tau_x, tau_s, ws, stages=G)
     for rep in range(3):
         o8 = _decode(P, L, x8, tau_x, tau_s, ws)
         assert all(np.array_equal(a, b) for a, b in zip(o8, ref8)), f"repeat {rep} (batch 8)"
-        o3 = _decode(P, L, x3, tau_x, tau_s, ws)
+        o3 = _decode(P, L, x3, tau_x, tau_s, ws, stages=G)
         assert all(np.array_equal(a, b) for a, b in zip(o3, ref3)), f"repeat {rep} (batch 3)"
+        p3 = _decode(P, L, x3, tau_x, tau_s, ws)  # per-token kernels on the same workspace
+        assert all(np.array_equal(a, b) for a, b in zip(p3[1:], ref3[1:])), f"repeat {rep} (batch 3 per-token)"
     bufs = _bufs(L, 8)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -217,6 +229,6 @@ def test_grouped_repeat_graph_and_workspace_reuse(P):
         torch.cuda.synchronize()
         got = [t.cpu().numpy() for t in bufs]
         assert all(np.array_equal(a, b) for a, b in zip(got, ref8)), f"graph replay {rep}"
-        o3 = _decode(P, L, x3, tau_x, tau_s, ws)  # eager work on the same workspace
+        o3 = _decode(P, L, x3, tau_x, tau_s, ws, stages=G)  # eager work on the same workspace
         assert all(np.array_equal(a, b) for a, b in zip(o3, ref3)), f"eager after replay {rep}"
     del g
