@@ -136,7 +136,6 @@ UpGateArgs upgate_args(const Plan& p, const prox_layer* L, const void* x, void* 
   UpGateArgs a;
   a.d = p.d;
   a.f = p.f;
-  a.max_cpb = p.ug_max_cpb;
   a.act = L->activation;
   a.w_upgate_t = L->w_upgate_t;
   a.x = x;
@@ -477,8 +476,10 @@ Plan make_plan(int d, int f, int wdtype) {
   p.rows_per_split = rps;
   p.splits = (d + rps - 1) / rps;
   // up/gate: enough 4-wave blocks for one kept channel per wave at ~30% keep
-  p.ug_blocks = std::max(64, f / 12);
-  p.ug_max_cpb = (f + p.ug_blocks - 1) / p.ug_blocks;
+  {  // up/gate: about one wave per 3 channels (at least 256 waves)
+    const int wpb = kUgThreads / 64;
+    p.ug_blocks = std::max(256 / wpb, f / (3 * wpb));
+  }
   // down: column slices of one wave-load, row groups to reach ~256 blocks of
   // 16 waves (few blocks keep the number of y atomics low)
   const int cw = 64 * (16 / static_cast<int>(elem_size(wdtype)));

@@ -15,6 +15,7 @@ namespace prox {
 constexpr int kThreads = 256;          // every kernel uses 4 waves of 64
 constexpr int kStage1Unroll = 16;      // proxy rows loaded per lane per batch
 constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads)
+constexpr int kUgThreads = 256;        // up/gate kernel: threads per block
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
 constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column slice
 constexpr int kBatchMax = 8;           // tokens per group of the batched kernels
@@ -34,7 +35,6 @@ struct Plan {
   int rows_per_split;
   // Stage 2 up/gate
   int ug_blocks;     // blocks per token
-  int ug_max_cpb;    // max channels per block
   // Stage 2 down
   int dn_col_slices; // ceil(d / column-slice width)
   int dn_row_groups;
@@ -90,7 +90,7 @@ struct DownBatchArgs {
 };
 
 struct UpGateArgs {
-  int d, f, max_cpb;
+  int d, f;
   int act;                // prox_activation
   const void* w_upgate_t; // [f][2][d]
   const void* x;          // [batch][d]
