@@ -11,12 +11,15 @@
 // gfx950 design:
 //   * upgate_batch_kernel: every block turns the tokens' Stage-1 bitmaps into
 //     the union channel list and the per-token index lists (block scans of
-//     the popcounts) for its slice of 16 union ordinals; two waves per 8
-//     channels split d in halves.  v_mfma_f32_16x16x32_bf16: A rows are the
-//     tokens' x (rows 8..15 zero), B columns are the up rows (0..7) and the
-//     gate rows (8..15) of the 8 channels, loaded straight from W^T (the
-//     contraction runs along a row, so each lane's 8 k-values are 16
-//     contiguous bytes).  A DPP rotate by 8 lanes brings g next to u.
+//     the popcounts) for its slice of 16 union ordinals; the slice is filled
+//     by whole waves, 32 lanes on the bits of one word at a time (a single
+//     lane walking a word's bits and tokens took longer than the weight
+//     stream).  Two waves per 8 channels split d in halves.
+//     v_mfma_f32_16x16x32_bf16: A rows are the tokens' x (rows 8..15 zero),
+//     B columns are the up rows (0..7) and the gate rows (8..15) of the 8
+//     channels, read from K-tiles of W^T staged in LDS (the contraction runs
+//     along a row, so each lane's 8 k-values are 16 contiguous bytes).  A DPP
+//     rotate by 8 lanes brings g next to u.
 //   * down_batch_kernel: a block owns a 512-column slice and a group of union
 //     ordinals; 32-row tiles of W_down (1 KB per row) are staged in LDS and
 //     ds_read_b64_tr_b16 turns them into B operands (8 rows of one column per
@@ -38,7 +41,6 @@ constexpr int kUgbChannels = 16;    // union channels per up/gate block (32 stag
 constexpr int kUgbKt = 512;         // K elements per staged tile (1 KB per row)
 constexpr int kUgbRowBytes = kUgbKt * 2 + 16;  // staged row stride
 constexpr int kUgbRowsPerThread = 2 * kUgbChannels / 4;  // 32 rows over 4 waves
-constexpr int kMaxWords = 8;        // bitmap words per thread (d_ff <= 65536)
 constexpr int kDnbThreads = 512;    // down: 8 waves x 64 columns
 constexpr int kDnbCols = 512;       // down: columns per block
 constexpr int kDnbTileRows = 32;    // down: rows per K-tile
@@ -59,8 +61,117 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 // ---------------------------------------------------------------------------
 // up/gate
 // ---------------------------------------------------------------------------
+// The union of a group's channel masks, as every up/gate block needs it: the
+// union ordinals [u0, u0 + kSlice) of this block go to s_ch (channel) and s_tb
+// (bit t set when token t keeps the channel) and to ulist; each token's index
+// list receives the entries of those channels; block 0 publishes U (at
+// ulist[f]) and every token's k_s.  Returns U.  The bitmap is read in passes
+// of one word per thread per token; a block scan of the 1 + nt popcounts
+// gives every word its union and per-token prefixes.  The slice is then
+// filled with all lanes of a wave on the 32 bits of one overlapping word at a
+// time (its data broadcast with readlane), not by the word's own thread.
+// The first pass's words come preloaded (union_words), so that a caller can
+// issue other loads behind them before the block's first barrier.
+template <int kNT>
+__device__ __forceinline__ void union_words(const UpGateBatchArgs& a, int pass, uint32_t (&tw)[kBatchMax]) {
+  const int nw = a.f / 32;
+  const int w = min(pass * kNT + static_cast<int>(threadIdx.x), nw - 1);
+#pragma unroll
+  for (int t = 0; t < kBatchMax; ++t)
+    tw[t] = reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(min(t, a.nt - 1)) * a.tok_bytes +
+                                              a.off_bitmap)[w];
+}
+
+template <int kNT, int kSlice>
+__device__ __forceinline__ int union_slice(const UpGateBatchArgs& a, int u0, int (&s_scan)[2][kNT / 64][1 + kBatchMax],
+                                           int* s_ch, uint32_t* s_tb, uint32_t (&tw)[kBatchMax]) {
+  constexpr int kW = kNT / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int f = a.f;
+  const int nt = a.nt;
+  const int nw = f / 32;
+  const int npass = (nw + kNT - 1) / kNT;
+  int* ulist = reinterpret_cast<int*>(a.ws + a.off_ulist);
+  int base[1 + kBatchMax];
+#pragma unroll
+  for (int q = 0; q <= kBatchMax; ++q) base[q] = 0;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int w = pass * kNT + tid;
+    if (pass > 0) union_words<kNT>(a, pass, tw);
+    uint32_t uw = 0u;
+    int cnt[1 + kBatchMax];
+#pragma unroll
+    for (int t = 0; t < kBatchMax; ++t) {
+      tw[t] = (t < nt && w < nw) ? tw[t] : 0u;
+      uw |= tw[t];
+      cnt[1 + t] = __popc(tw[t]);
+    }
+    cnt[0] = __popc(uw);
+    int inc[1 + kBatchMax];
+#pragma unroll
+    for (int q = 0; q <= kBatchMax; ++q) inc[q] = wave_inclusive_scan_int(cnt[q]);
+    if (lane == 63) {
+#pragma unroll
+      for (int q = 0; q <= kBatchMax; ++q) s_scan[pass & 1][wave][q] = inc[q];
+    }
+    __syncthreads();
+    int excl[1 + kBatchMax];
+#pragma unroll
+    for (int q = 0; q <= kBatchMax; ++q) {
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int v = 0; v < kW; ++v) {
+        const int c = s_scan[pass & 1][v][q];
+        pre += v < wave ? c : 0;
+        tot += c;
+      }
+      excl[q] = base[q] + pre + inc[q] - cnt[q];
+      base[q] += tot;
+    }
+    // words of this wave that hold ordinals of the slice, one at a time
+    uint64_t ovm = __ballot(cnt[0] > 0 && excl[0] < u0 + kSlice && excl[0] + cnt[0] > u0);
+    while (ovm) {  // wave-uniform
+      const int src = static_cast<int>(__builtin_ctzll(ovm));
+      ovm &= ovm - 1ull;
+      const uint32_t su = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(uw), src));
+      const int se = __builtin_amdgcn_readlane(excl[0], src);
+      uint32_t st[kBatchMax];
+      int sx[kBatchMax];
+#pragma unroll
+      for (int t = 0; t < kBatchMax; ++t) {
+        st[t] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw[t]), src));
+        sx[t] = __builtin_amdgcn_readlane(excl[1 + t], src);
+      }
+      const int bit = lane & 31;
+      const uint32_t below = (1u << bit) - 1u;
+      const int o = se + __popc(su & below);
+      if (lane < 32 && ((su >> bit) & 1u) && o >= u0 && o < u0 + kSlice) {
+        const int j = (pass * kNT + wave * 64 + src) * 32 + bit;
+        uint32_t tb = 0u;
+#pragma unroll
+        for (int t = 0; t < kBatchMax; ++t) {
+          if ((st[t] >> bit) & 1u) {
+            tb |= 1u << t;
+            a.mask_idx[static_cast<size_t>(t) * f + sx[t] + __popc(st[t] & below)] = j;
+          }
+        }
+        s_ch[o - u0] = j;
+        s_tb[o - u0] = tb;
+        ulist[o] = j;
+      }
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    ulist[f] = base[0];
+    for (int t = 0; t < nt; ++t) a.mask_count[t] = base[1 + t];
+  }
+  return base[0];
+}
+
 __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs a) {
-  __shared__ int s_scan[4][1 + kBatchMax];
+  __shared__ int s_scan[2][kThreads / 64][1 + kBatchMax];
   __shared__ int s_ch[kUgbChannels];
   __shared__ uint32_t s_tb[kUgbChannels];
   __shared__ float s_red[2][64][4];
@@ -71,107 +182,15 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int d = a.d;
-  const int f = a.f;
   const int nt = a.nt;
-  const int nw = f / 32;
-  const int per = (nw + kThreads - 1) / kThreads;
-  const int w0 = min(nw, tid * per);
 
-  // ---- union and per-token counts of this thread's bitmap words
-  uint32_t uw[kMaxWords];
-  int cnt[1 + kBatchMax];
-#pragma unroll
-  for (int q = 0; q <= kBatchMax; ++q) cnt[q] = 0;
-#pragma unroll
-  for (int k = 0; k < kMaxWords; ++k) uw[k] = 0u;
-#pragma unroll
-  for (int t = 0; t < kBatchMax; ++t) {
-    if (t >= nt) break;
-    const uint32_t* bm = reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_bitmap);
-    uint32_t wv[kMaxWords];
-#pragma unroll
-    for (int k = 0; k < kMaxWords; ++k) wv[k] = bm[min(w0 + k, nw - 1)];
-#pragma unroll
-    for (int k = 0; k < kMaxWords; ++k) {
-      const uint32_t v = (k < per && w0 + k < nw) ? wv[k] : 0u;
-      uw[k] |= v;
-      cnt[1 + t] += __popc(v);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kMaxWords; ++k) cnt[0] += __popc(uw[k]);
-
-  // ---- block scan of the 1 + nt counts (exclusive prefix per thread)
-  int inc[1 + kBatchMax];
-#pragma unroll
-  for (int q = 0; q <= kBatchMax; ++q) inc[q] = wave_inclusive_scan_int(cnt[q]);
-  if (lane == 63) {
-#pragma unroll
-    for (int q = 0; q <= kBatchMax; ++q) s_scan[wave][q] = inc[q];
-  }
-  __syncthreads();
-  int excl[1 + kBatchMax], total[1 + kBatchMax];
-#pragma unroll
-  for (int q = 0; q <= kBatchMax; ++q) {
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += s_scan[w][q];
-    excl[q] = base + inc[q] - cnt[q];
-    total[q] = (s_scan[0][q] + s_scan[1][q]) + (s_scan[2][q] + s_scan[3][q]);
-  }
-  const int U = total[0];
-  int* ulist = reinterpret_cast<int*>(a.ws + a.off_ulist);
-  if (blockIdx.x == 0 && tid == 0) {
-    ulist[f] = U;
-    for (int t = 0; t < nt; ++t) a.mask_count[t] = total[1 + t];
-  }
   const int u0 = static_cast<int>(blockIdx.x) * kUgbChannels;
+  uint32_t tw[kBatchMax];
+  union_words<kThreads>(a, 0, tw);
+  const int U = union_slice<kThreads, kUgbChannels>(a, u0, s_scan, s_ch, s_tb, tw);
   if (u0 >= U) return;  // block-uniform
   const int u1 = min(U, u0 + kUgbChannels);
   const int nloc = u1 - u0;
-
-  // ---- the slice's channels, their token bits and the index-list entries
-  if (excl[0] < u1 && excl[0] + cnt[0] > u0) {
-    int o = excl[0];
-    int ot[kBatchMax];
-#pragma unroll
-    for (int t = 0; t < kBatchMax; ++t) ot[t] = excl[1 + t];
-    for (int k = 0; k < per && w0 + k < nw; ++k) {
-      const int w = w0 + k;
-      uint32_t tw[kBatchMax];
-#pragma unroll
-      for (int t = 0; t < kBatchMax; ++t)
-        tw[t] = t < nt ? reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(t) * a.tok_bytes +
-                                                           a.off_bitmap)[w]
-                       : 0u;
-      uint32_t bits = uw[k];
-      if (o < u1 && o + __popc(bits) > u0) {
-        while (bits) {
-          const int bit = __ffs(bits) - 1;
-          bits &= bits - 1u;
-          if (o >= u0 && o < u1) {
-            const int j = w * 32 + bit;
-            const uint32_t below = (1u << bit) - 1u;
-            uint32_t tb = 0u;
-#pragma unroll
-            for (int t = 0; t < kBatchMax; ++t) {
-              if ((tw[t] >> bit) & 1u) {
-                tb |= 1u << t;
-                a.mask_idx[static_cast<size_t>(t) * f + ot[t] + __popc(tw[t] & below)] = j;
-              }
-            }
-            s_ch[o - u0] = j;
-            s_tb[o - u0] = tb;
-            ulist[o] = j;
-          }
-          ++o;
-        }
-      } else {
-        o += __popc(bits);
-      }
-#pragma unroll
-      for (int t = 0; t < kBatchMax; ++t) ot[t] += __popc(tw[t]);
-    }
-  }
   __syncthreads();
 
   // ---- MFMA: wave -> (channel half ch = wave & 1, K half kh = wave >> 1)
