@@ -318,20 +318,37 @@ __global__ __launch_bounds__(kDnbThreads) void down_batch_kernel(DownBatchArgs a
   int* ul = reinterpret_cast<int*>(As + static_cast<size_t>(a.max_rows) * 16);
   for (int r = tid; r < nr; r += kDnbThreads) ul[r] = min(max(ulist[o0 + r], 0), f - 1);
   __syncthreads();
-  // A: rows r of the group, m = 2t + part: s_t[ul[r]] split into bf16 hi and lo
-  for (int idx = tid; idx < ntile * kDnbTileRows * kBatchMax; idx += kDnbThreads) {
-    const int r = idx / kBatchMax;
-    const int t = idx % kBatchMax;
-    float s = 0.f;
-    if (r < nr && t < nt)
-      s = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_ssp)[ul[r]];
-    const uint16_t hi = f32_to_bf16_rne(s);
-    const uint16_t lo = f32_to_bf16_rne(s - __uint_as_float(static_cast<uint32_t>(hi) << 16));
-    const int kt = r / kDnbTileRows;
-    const int k = r % kDnbTileRows;
-    uint16_t* at = As + static_cast<size_t>(kt) * 512 + ((k >> 3) * 16) * 8 + (k & 7);
-    at[(2 * t) * 8] = hi;
-    at[(2 * t + 1) * 8] = lo;
+  // A: rows r of the group, m = 2t + part: s_t[ul[r]] split into bf16 hi and
+  // lo.  The gathers of 8 entries per thread are issued before any is used,
+  // so the fill costs one memory round trip per 8 entries, not one per entry.
+  constexpr int kAfill = 8;
+  const int nidx = ntile * kDnbTileRows * kBatchMax;
+  for (int i0 = 0; i0 < nidx; i0 += kAfill * kDnbThreads) {  // block-uniform
+    float sv[kAfill];
+#pragma unroll
+    for (int u = 0; u < kAfill; ++u) {
+      const int idx = i0 + u * kDnbThreads + tid;
+      const int r = idx / kBatchMax;
+      const int t = idx % kBatchMax;
+      sv[u] = (idx < nidx && r < nr && t < nt)
+                  ? reinterpret_cast<const float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_ssp)[ul[r]]
+                  : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kAfill; ++u) {
+      const int idx = i0 + u * kDnbThreads + tid;
+      if (idx < nidx) {
+        const int r = idx / kBatchMax;
+        const int t = idx % kBatchMax;
+        const uint16_t hi = f32_to_bf16_rne(sv[u]);
+        const uint16_t lo = f32_to_bf16_rne(sv[u] - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+        const int kt = r / kDnbTileRows;
+        const int k = r % kDnbTileRows;
+        uint16_t* at = As + static_cast<size_t>(kt) * 512 + ((k >> 3) * 16) * 8 + (k & 7);
+        at[(2 * t) * 8] = hi;
+        at[(2 * t + 1) * 8] = lo;
+      }
+    }
   }
 
   // staging: thread -> (16-B unit u = tid % 64, rows tid / 64 + 8q); unit u of
