@@ -475,7 +475,6 @@ Plan make_plan(int d, int f, int wdtype) {
   rps = std::min(rps, 2048);  // bounds the LDS list of kept rows (20 B per row)
   p.rows_per_split = rps;
   p.splits = (d + rps - 1) / rps;
-  // up/gate: enough 4-wave blocks for one kept channel per wave at ~30% keep
   {  // up/gate: about one wave per 3 channels (at least 256 waves)
     const int wpb = kUgThreads / 64;
     p.ug_blocks = std::max(256 / wpb, f / (3 * wpb));

@@ -194,6 +194,22 @@ def test_decode_ragged_small_shapes(P):
         _run_decode(P, L, layer, ov, [0, 1, 2], tau_x, tau_s, f"{d}x{f}-{dt}")
 
 
+def test_decode_wide_dff_bitmap_chunks(P):
+    """d_ff = 33024: the up/gate waves hold the first two 16384-channel chunks
+    of the Stage-1 bitmap in registers and read the third from memory when
+    they count and select; the all-pass case gives each wave three ordinals
+    (the later ones re-read every chunk), and both batch 1 and a group of
+    four (grouped kernels, union passes over 1032 bitmap words)."""
+    layer = synth.make_layer(_small_cfg(128, 33024, "bf16", 45), n_dec=4)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov)
+    _run_decode(P, L, layer, ov, [0], tau_x, tau_s, "128x33024")
+    _run_decode(P, L, layer, ov, [1, 2, 3, 0], tau_x, tau_s, "128x33024-b4")
+    y, mi, mc, ic = _run_decode(P, L, layer, ov, [2], 0.0, 0.0, "128x33024-all-pass")
+    assert mc[0] == L.d_ff and np.array_equal(mi[0], np.arange(L.d_ff))
+
+
 def test_decode_degenerate_thresholds(P):
     layer, ov = oracle_layer("tiny")
     L = pack_layer(layer)
