@@ -19,10 +19,11 @@
 //     for both proxies, then gathers those rows; no block barrier precedes
 //     the gather.
 //   * main loop: 8 lanes cover one kept row's 128-byte slice (16 up + 16
-//     gate codes per lane, one 16-B load); each lane keeps 8 loads
-//     outstanding; x and the two scales of a row are fetched in one round
-//     trip.  Rejected rows are never
-//     touched, so the bytes read are k_x * panel width per panel.
+//     gate codes per lane, one 16-B load); each lane keeps 16 loads
+//     outstanding, so a wave's 128 rows (at 512 rows per split) go out in
+//     one batch; x and the two scales of a row are fetched in one round
+//     trip.  Rejected rows are never touched, so the bytes read are
+//     k_x * panel width per panel.
 //   * INT4 unpack: a nibble masked into the low 10 bits of a half word is an
 //     f16 subnormal equal to nibble * 2^-24 (or 16 * nibble * 2^-24 for the
 //     high nibble of a byte).  v_fma_mix_f32 widens it exactly and fuses the
