@@ -19,7 +19,7 @@ constexpr int kUgThreads = 256;        // up/gate kernel: threads per block
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
 constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column slice
 constexpr int kBatchMax = 8;           // tokens per group of the batched kernels
-constexpr int kGroupedMinTokens = 4;   // smaller groups run the per-token kernels (faster there)
+constexpr int kGroupedMinTokens = 3;   // smaller groups run the per-token kernels (faster there)
 
 // ---------------------------------------------------------------------------
 // Per-launch plan (host-computed, passed by value to kernels)

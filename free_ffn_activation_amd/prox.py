@@ -31,7 +31,7 @@ PROX_STAGE_PROXY = 1
 PROX_STAGE_UPGATE = 2
 PROX_STAGE_DOWN = 4
 PROX_STAGE_PER_TOKEN = 8  # batch >= 2: per-token kernels for every group
-PROX_STAGE_GROUPED = 16   # batch >= 2: grouped kernels for every group (default: groups of >= 4 tokens)
+PROX_STAGE_GROUPED = 16   # batch >= 2: grouped kernels for every group (default: groups of >= 3 tokens)
 
 _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPORTED",
                  -3: "PROX_ERR_HIP", -4: "PROX_ERR_INTERNAL"}

@@ -248,7 +248,7 @@ prox_status prox_calibrate_hist(const prox_layer* layer, const void* X_cal, int3
  *   in_count    device [batch] int32 (k_x per token) or NULL
  *   ws          device, >= prox_workspace_size(batch) bytes, zeroed once
  * Asynchronous: kernels on `stream`, no host synchronisation.  batch 1 runs
- * three kernels.  batch >= 2 runs groups of up to 8 tokens; a group of 4 or
+ * three kernels.  batch >= 2 runs groups of up to 8 tokens; a group of 3 or
  * more tokens runs the grouped kernels, a smaller one the per-token kernels
  * (prox_ffn_decode_stages can force either).  Grouped (the pages study
  * batch 1 and leave larger batches open, [blog] limitations section): Stage 1
@@ -294,7 +294,7 @@ prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32
  * and channels) for every group; same results up to fp32 summation order */
 #define PROX_STAGE_PER_TOKEN 8
 /* with batch >= 2: run the grouped kernels for every group (by default a group
- * of fewer than 4 tokens runs the per-token kernels, which are faster there);
+ * of fewer than 3 tokens runs the per-token kernels, which are faster there);
  * not together with PROX_STAGE_PER_TOKEN */
 #define PROX_STAGE_GROUPED 16
 prox_status prox_ffn_decode_stages(const prox_layer* layer, const void* x, int32_t batch,

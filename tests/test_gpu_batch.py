@@ -1,7 +1,7 @@
 """GPU parity of the grouped batch path (2..8 tokens per group, more tokens in
 several groups): Stage 1 over the union of the group's kept rows on the matrix
 cores, Stage 2 over the union of the channel lists (bf16 weights).  By default
-groups of fewer than 4 tokens run the per-token kernels; PROX_STAGE_GROUPED
+groups of fewer than 3 tokens run the per-token kernels; PROX_STAGE_GROUPED
 forces the grouped ones so that small groups are covered too.
 
 Every token is checked against the CPU oracle run on that token alone (the
@@ -100,7 +100,7 @@ def test_grouped_decode_parity(P, d, f, dtype, batch, seed):
     _check_tokens(ov, ov["x_dec"], out, tau_x, tau_s, f"{d}x{f}-{dtype}-b{batch}")
     forced = _decode(P, L, x, tau_x, tau_s, ws, stages=7 | P.PROX_STAGE_GROUPED)
     _check_tokens(ov, ov["x_dec"], forced, tau_x, tau_s, f"{d}x{f}-{dtype}-b{batch}-grouped")
-    if batch < 4:  # the default ran the per-token kernels: same lists as forcing them
+    if batch < 3:  # the default ran the per-token kernels: same lists as forcing them
         pt = _decode(P, L, x, tau_x, tau_s, ws, stages=7 | P.PROX_STAGE_PER_TOKEN)
         assert all(np.array_equal(a, b) for a, b in zip(out[1:], pt[1:]))
         # y: the per-token down kernel sums with atomics, so only up to fp32 order
