@@ -107,6 +107,20 @@ def test_grouped_decode_parity(P, d, f, dtype, batch, seed):
         assert y_errors(out[0], pt[0].astype(np.float64))[1] <= 1e-5
 
 
+@pytest.mark.parametrize("d,f,batch,seed", [(512, 1024, 4, 91), (576, 1152, 8, 92)])
+def test_grouped_geglu_parity(P, d, f, batch, seed):
+    """A GeGLU layer (GELU-tanh gate) on the grouped kernels: the gate in the
+    grouped Stage-1 activation and in the grouped up/gate epilogue."""
+    layer = synth.make_layer(_cfg(d, f, "bf16", seed, batch), n_dec=batch)
+    ov = oracle_view(layer)
+    L = pack_layer(layer, activation=P.PROX_ACT_GELU_TANH)
+    tau_x, tau_s = _taus(ov, act="gelu_tanh")
+    x = to_device(layer.x_dec, "bf16")
+    ws = P.new_workspace(d, f, batch)
+    out = _decode(P, L, x, tau_x, tau_s, ws)
+    _check_tokens(ov, ov["x_dec"], out, tau_x, tau_s, f"geglu-{d}x{f}-b{batch}", act="gelu_tanh")
+
+
 def test_grouped_qwen3_8b_batch8_and_per_token_kernels(P):
     """The batch-8 Qwen3-8B-shaped layer: grouped path against the oracle, and
     against the per-token kernels on the same inputs."""
