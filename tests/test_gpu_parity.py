@@ -210,6 +210,18 @@ def test_decode_wide_dff_bitmap_chunks(P):
     assert mc[0] == L.d_ff and np.array_equal(mi[0], np.arange(L.d_ff))
 
 
+def test_decode_max_d_model(P):
+    """d_model = 12288, the largest shape: every up/gate thread stages its six
+    16-byte chunks of x, a channel's run takes three 8-step load batches, the
+    down kernel covers 24 column slices; batch 1 and a grouped batch of 3."""
+    layer = synth.make_layer(_small_cfg(12288, 256, "bf16", 46), n_dec=4)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov)
+    _run_decode(P, L, layer, ov, [0], tau_x, tau_s, "12288x256")
+    _run_decode(P, L, layer, ov, [1, 2, 3], tau_x, tau_s, "12288x256-b3")
+
+
 def test_decode_degenerate_thresholds(P):
     layer, ov = oracle_layer("tiny")
     L = pack_layer(layer)
