@@ -55,7 +55,9 @@ struct KeptA {
   float u24, u20, g24, g20;
 };
 
-constexpr int kRedStride = kThreads + 1;  // LDS row of the cross-slot reduction
+// LDS row of the cross-slot reduction: a stride of 2 mod 32 words puts the 32
+// reads of a half-wave (16 columns x 2 chunks) in 32 distinct banks
+constexpr int kRedStride = kThreads + 2;
 
 // Adds the 8 proxy columns packed in one dword (byte b: column 2b in the low
 // nibble, 2b+1 in the high nibble; nibble = code + 8) times `a`, where

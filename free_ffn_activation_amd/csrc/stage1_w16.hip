@@ -27,7 +27,7 @@ constexpr int kW16Pw = 128;                    // panel width (output columns)
 constexpr int kW16Lpr = 8;                     // lanes per row (one 64-byte chunk each)
 constexpr int kW16WaveSlots = 64 / kW16Lpr;    // rows per wave step
 constexpr int kW16Rows = 4;                    // rows per lane slot in flight
-constexpr int kW16RedStride = kThreads + 1;
+constexpr int kW16RedStride = kThreads + 2;  // conflict-free reduction reads (2 mod 32 words)
 
 __device__ __forceinline__ void acc_bf16x8(float* acc, const u32x4_t& w, float a) {
   acc[0] = fmaf(a, bf16lo(w.x), acc[0]);
