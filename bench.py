@@ -245,7 +245,9 @@ def main() -> int:
 
     # ---------------------------------------------------------------- graph timing
     def time_graph(fn, label):
-        g = torch.cuda.CUDAGraph()
+        """Exactly K steps replayed from HIP graphs (the rotation of
+        steps_per_round steps K // steps_per_round times, then its first
+        K % steps_per_round steps), bracketed by HIP events."""
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
@@ -253,27 +255,35 @@ def main() -> int:
                 fn(s)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for s in range(steps_per_round):
-                fn(s)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, int(math.ceil(K / steps_per_round)))
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(n):
+                    fn(s)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            return g
+
+        full, tail = divmod(K, steps_per_round)
+        g_full = capture(steps_per_round) if full else None
+        g_tail = capture(tail) if tail else None
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
         ev0.record()
-        for _ in range(reps):
-            g.replay()
+        for _ in range(full):
+            g_full.replay()
+        if g_tail is not None:
+            g_tail.replay()
         ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
-        us = ev0.elapsed_time(ev1) * 1e3 / (reps * steps_per_round)
-        log(f"{label}: {us:.2f} us/layer over {reps * steps_per_round} graph-replayed steps "
-            f"(wall {wall * 1e3:.1f} ms)")
-        del g
-        return us, reps * steps_per_round, wall
+        us = ev0.elapsed_time(ev1) * 1e3 / K
+        log(f"{label}: {us:.2f} us/layer over {K} graph-replayed steps (wall {wall * 1e3:.1f} ms)")
+        del g_full, g_tail
+        return us, K, wall
 
     if args.no_graph:
         prox_us, timed_steps, wall = eager_us, K, None
