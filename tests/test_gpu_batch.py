@@ -121,6 +121,23 @@ def test_grouped_geglu_parity(P, d, f, batch, seed):
     _check_tokens(ov, ov["x_dec"], out, tau_x, tau_s, f"geglu-{d}x{f}-b{batch}", act="gelu_tanh")
 
 
+def test_many_groups_batch43(P):
+    """43 tokens: five grouped groups of 8 and a grouped tail of 3, every
+    token against the oracle; the same call with the per-token kernels forced
+    gives the same k_x and index lists outside the tau_s band."""
+    d, f, batch = 256, 512, 43
+    layer = synth.make_layer(_cfg(d, f, "bf16", 93, batch), n_dec=batch)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _taus(ov)
+    x = to_device(layer.x_dec, "bf16")
+    ws = P.new_workspace(d, f, batch)
+    out = _decode(P, L, x, tau_x, tau_s, ws)
+    _check_tokens(ov, ov["x_dec"], out, tau_x, tau_s, "256x512-b43")
+    pt = _decode(P, L, x, tau_x, tau_s, ws, stages=7 | P.PROX_STAGE_PER_TOKEN)
+    assert np.array_equal(out[3], pt[3])  # k_x
+
+
 def test_grouped_qwen3_8b_batch8_and_per_token_kernels(P):
     """The batch-8 Qwen3-8B-shaped layer: grouped path against the oracle, and
     against the per-token kernels on the same inputs."""
