@@ -432,22 +432,22 @@ __global__ __launch_bounds__(kDnbThreads) void down_batch_kernel(DownBatchArgs a
   }
 }
 
+// kG >= a.groups: every group's partial is loaded unconditionally (indices
+// past the last group re-read it and are not added), so all loads are in
+// flight before the first use; the sum keeps the fixed group order.
+template <int kG>
 __global__ __launch_bounds__(kThreads) void down_reduce_kernel(DownBatchArgs a, float* y) {
   const int idx = blockIdx.x * kThreads + threadIdx.x;
   if (idx >= a.nt * a.d) return;
   const int t = idx / a.d;
   const int c = idx - t * a.d;
   const float* dp = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_dpart) + c;
-  // every group's partial is in flight at once (groups <= kDnbMaxGroups);
-  // the sum keeps the fixed group order
-  float v[kDnbMaxGroups];
+  float v[kG];
 #pragma unroll
-  for (int u = 0; u < kDnbMaxGroups; ++u)
-    if (u < a.groups) v[u] = dp[static_cast<size_t>(u) * a.d];
+  for (int u = 0; u < kG; ++u) v[u] = dp[static_cast<size_t>(min(u, a.groups - 1)) * a.d];
   float s = 0.f;
 #pragma unroll
-  for (int u = 0; u < kDnbMaxGroups; ++u)
-    if (u < a.groups) s += v[u];
+  for (int u = 0; u < kG; ++u) s += u < a.groups ? v[u] : 0.f;
   y[idx] = s;
 }
 
@@ -470,8 +470,15 @@ hipError_t launch_down_batch(const DownBatchArgs& a, float* y, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.nt * a.d;
-  hipLaunchKernelGGL(down_reduce_kernel, dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, s, a, y);
+  const dim3 rgrid(static_cast<unsigned>((n + kThreads - 1) / kThreads));
+  if (a.groups <= 8)
+    hipLaunchKernelGGL(down_reduce_kernel<8>, rgrid, dim3(kThreads), 0, s, a, y);
+  else if (a.groups <= 16)
+    hipLaunchKernelGGL(down_reduce_kernel<16>, rgrid, dim3(kThreads), 0, s, a, y);
+  else if (a.groups <= 32)
+    hipLaunchKernelGGL(down_reduce_kernel<32>, rgrid, dim3(kThreads), 0, s, a, y);
+  else
+    hipLaunchKernelGGL(down_reduce_kernel<kDnbMaxGroups>, rgrid, dim3(kThreads), 0, s, a, y);
   return hipGetLastError();
 }
 
