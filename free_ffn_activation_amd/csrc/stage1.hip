@@ -276,15 +276,16 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
       bitmap[w0 + 1] = static_cast<uint32_t>(bal >> 32);
     }
   }
-  if (tid == 0) {
-    // ready for the next stream-ordered call
-    __hip_atomic_store(&tickets[panel], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (panel == 0 && a.in_count != nullptr) {
-      int t = 0;
-      for (int k = 0; k < a.splits; ++k)
-        t += __hip_atomic_load(&kcount[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      a.in_count[b] = t;
-    }
+  // ready for the next stream-ordered call
+  if (tid == 0) __hip_atomic_store(&tickets[panel], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (panel == 0 && a.in_count != nullptr && wave == 0) {
+    // k_x: one split count per lane (splits <= 64), summed across the wave,
+    // so the loads make one round trip
+    const int kc = lane < a.splits
+                       ? __hip_atomic_load(&kcount[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0;
+    const int t = wave_sum_int(kc);
+    if (lane == 0) a.in_count[b] = t;
   }
 }
 
