@@ -58,6 +58,8 @@ struct KeptA {
 // LDS row of the cross-slot reduction: a stride of 2 mod 32 words puts the 32
 // reads of a half-wave (16 columns x 2 chunks) in 32 distinct banks
 constexpr int kRedStride = kThreads + 2;
+// kept-row lists are sized in whole gather batches (128 rows at kPw 128, 64 at 256)
+constexpr int kS1ListBatch = 128;
 
 // Adds the 8 proxy columns packed in one dword (byte b: column 2b in the low
 // nibble, 2b+1 in the high nibble; nibble = code + 8) times `a`, where
@@ -110,11 +112,18 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   // barrier is needed before the gather starts.
   const int row0 = split * a.rows_per_split;
   const int row1 = min(d, row0 + a.rows_per_split);
+  constexpr int kWaveSlots = 64 / kLpr;                    // rows in flight per wave load
+  constexpr int kBatchRows = kWaveSlots * kStage1Unroll;    // rows per gather batch
   const int wchunk = (a.rows_per_split + 3) / 4;
-  const int wcap = wchunk + 1;  // one zero-weight sentinel entry per wave
+  // the lists hold whole batches: positions past the last kept row up to the
+  // batch end are zero-weight sentinels that read row 0
+  const int wcap = (wchunk + kS1ListBatch - 1) / kS1ListBatch * kS1ListBatch;
+  const int ucap = wcap / kWaveSlots;
   const int wr0 = min(row1, row0 + wave * wchunk);
   const int wr1 = min(row1, wr0 + wchunk);
   KeptA* ka = reinterpret_cast<KeptA*>(smem) + wave * wcap;
+  // row byte offsets, transposed: position p at koff[(p % kWaveSlots) * ucap +
+  // p / kWaveSlots], so the offsets a lane gathers in one batch are contiguous
   uint32_t* koff = reinterpret_cast<uint32_t*>(reinterpret_cast<KeptA*>(smem) + 4 * wcap) + wave * wcap;
   constexpr float k2p24 = 16777216.0f;
   constexpr float k2p20 = 1048576.0f;
@@ -142,16 +151,17 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
       if (keep) {
         const int pos = nkept + __popcll(bal & ((1ull << lane) - 1ull));
         ka[pos] = KeptA{au * k2p24, au * k2p20, ag * k2p24, ag * k2p20};
-        koff[pos] = static_cast<uint32_t>(i) * static_cast<uint32_t>(a.proxy_stride);
+        koff[(pos % kWaveSlots) * ucap + pos / kWaveSlots] = static_cast<uint32_t>(i) * static_cast<uint32_t>(a.proxy_stride);
       }
       nkept += __popcll(bal);
       sum_up += au;
       sum_gate += ag;
     }
   }
-  if (lane == 0) {  // slots past the end read row 0 with weight 0
-    ka[nkept] = KeptA{0.f, 0.f, 0.f, 0.f};
-    koff[nkept] = 0u;
+  // sentinels up to the end of the last batch
+  for (int p = nkept + lane; p < (nkept + kBatchRows - 1) / kBatchRows * kBatchRows; p += 64) {
+    ka[p] = KeptA{0.f, 0.f, 0.f, 0.f};
+    koff[(p % kWaveSlots) * ucap + p / kWaveSlots] = 0u;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -167,34 +177,42 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   // ---- main loop over the wave's kept rows: kLpr lanes per row
   const int wslot = lane / kLpr;
   const int chunk = lane % kLpr;
-  const uint8_t* pbase = a.proxy_q + static_cast<size_t>(panel) * kPw + chunk * 16;
+  const uint8_t* qbase = a.proxy_q + static_cast<size_t>(panel) * kPw;  // uniform; 32-bit offsets below
+  const uint32_t coff = static_cast<uint32_t>(chunk * 16);
   float acc_u[16], acc_g[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     acc_u[e] = 0.f;
     acc_g[e] = 0.f;
   }
-  constexpr int kWaveSlots = 64 / kLpr;
-  // One batch covers kWaveSlots * kStage1Unroll = 128 rows, a wave's whole
-  // share at 512 rows per split, so every wave makes a single round trip.
-  // Loads are unconditional (slots past the end read the sentinel row) so the
-  // compiler can wait on them one at a time; a = x_i * scale_i comes from LDS
-  // at use, and steps with no kept row in any slot are skipped.
-  for (int r0 = wslot; r0 < nkept; r0 += kWaveSlots * kStage1Unroll) {
-    const int rb = r0 - wslot;  // wave-uniform base of this batch
+  // One batch covers kBatchRows = 128 rows (kPw 128), a wave's whole share
+  // at 512 rows per split, so every wave makes a single round trip.  The
+  // batch's offsets come from LDS as 16-byte vectors, then all its loads are
+  // issued (sentinel slots read row 0); a = x_i * scale_i of the next row is
+  // read from LDS while the current row is added, and steps with no kept row
+  // in any slot are skipped.
+  for (int rb = 0; rb < nkept; rb += kBatchRows) {  // wave-uniform
+    const uint32_t* ko = koff + wslot * ucap + rb / kWaveSlots;
+    uint32_t off[kStage1Unroll];
+#pragma unroll
+    for (int u = 0; u < kStage1Unroll; ++u) off[u] = ko[u];
     uint4 w[kStage1Unroll];
 #pragma unroll
-    for (int u = 0; u < kStage1Unroll; ++u) w[u] = ldg16(pbase + koff[min(r0 + u * kWaveSlots, nkept)]);
+    for (int u = 0; u < kStage1Unroll; ++u) w[u] = ldg16(qbase + (off[u] + coff));
     __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
+    const KeptA* kb = ka + rb + wslot;
+    KeptA cur = kb[0];
 #pragma unroll
     for (int u = 0; u < kStage1Unroll; ++u) {
+      KeptA nxt = cur;
+      if (u + 1 < kStage1Unroll) nxt = kb[(u + 1) * kWaveSlots];
       if (rb + u * kWaveSlots < nkept) {
-        const KeptA av = ka[min(r0 + u * kWaveSlots, nkept)];
-        acc_dword(acc_u + 0, w[u].x, av.u24, av.u20);
-        acc_dword(acc_u + 8, w[u].y, av.u24, av.u20);
-        acc_dword(acc_g + 0, w[u].z, av.g24, av.g20);
-        acc_dword(acc_g + 8, w[u].w, av.g24, av.g20);
+        acc_dword(acc_u + 0, w[u].x, cur.u24, cur.u20);
+        acc_dword(acc_u + 8, w[u].y, cur.u24, cur.u20);
+        acc_dword(acc_g + 0, w[u].z, cur.g24, cur.g20);
+        acc_dword(acc_g + 8, w[u].w, cur.g24, cur.g20);
       }
+      cur = nxt;
     }
   }
 
@@ -295,8 +313,8 @@ hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_
                          hipStream_t s) {
   if (a.proxy_kind == PROX_PROXY_W16) return launch_stage1_w16(a, batch, write_state, s);
   const dim3 grid(static_cast<unsigned>(a.n_panels * a.splits), static_cast<unsigned>(batch));
-  const size_t kept_bytes =
-      static_cast<size_t>(a.rows_per_split + 4) * (sizeof(KeptA) + sizeof(uint32_t));
+  const size_t wcap = static_cast<size_t>(((a.rows_per_split + 3) / 4 + kS1ListBatch - 1) / kS1ListBatch) * kS1ListBatch;
+  const size_t kept_bytes = 4 * wcap * (sizeof(KeptA) + sizeof(uint32_t));
   const size_t red_bytes = static_cast<size_t>(32) * kRedStride * sizeof(float);
   const size_t smem = kept_bytes > red_bytes ? kept_bytes : red_bytes;
 #define PROX_S1_LAUNCH(TAG, WS, PW) \
