@@ -55,11 +55,24 @@ struct KeptA {
   float u24, u20, g24, g20;
 };
 
+// Stage-1 block: 4 waves, each taking a quarter of the split's rows;
+// kS1Unroll proxy rows per lane per batch.  (8 waves of 8 rows per lane were
+// slower: the shorter batches leave less in flight per wave.)
+constexpr int kS1Threads = kThreads;
+constexpr int kS1Waves = kS1Threads / 64;
+constexpr int kS1Unroll = 16;
+constexpr int kS1Pw = 128;                       // panel width (output columns)
+constexpr int kS1Lpr = kS1Pw / 16;               // lanes per row (16 columns each)
+constexpr int kS1WaveSlots = 64 / kS1Lpr;        // rows in flight per wave load
+constexpr int kS1BatchRows = kS1WaveSlots * kS1Unroll;
+// kept-row lists are sized in whole gather batches
+__host__ __device__ constexpr int s1_wave_cap(int rows_per_split) {
+  return ((rows_per_split + kS1Waves - 1) / kS1Waves + kS1BatchRows - 1) / kS1BatchRows * kS1BatchRows;
+}
+constexpr int kS1RedSlots = kS1Threads / kS1Lpr;  // row slots reduced through LDS
 // LDS row of the cross-slot reduction: a stride of 2 mod 32 words puts the 32
 // reads of a half-wave (16 columns x 2 chunks) in 32 distinct banks
-constexpr int kRedStride = kThreads + 2;
-// kept-row lists are sized in whole gather batches (128 rows at kPw 128, 64 at 256)
-constexpr int kS1ListBatch = 128;
+constexpr int kRedStride = kS1RedSlots * kS1Lpr + 2;
 
 // Adds the 8 proxy columns packed in one dword (byte b: column 2b in the low
 // nibble, 2b+1 in the high nibble; nibble = code + 8) times `a`, where
@@ -80,14 +93,13 @@ __device__ __forceinline__ void acc_dword(float* acc, uint32_t w, float a24, flo
   acc[7] = fmaf(a20, static_cast<float>(h3.y), acc[7]);
 }
 
-template <typename T, bool kWriteState, int kPw>
-__global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
-  constexpr int kLpr = kPw / 16;             // lanes per row (16 columns each)
-  constexpr int kSlots = kThreads / kLpr;    // row slots per block
-  constexpr int kNout = 2 * kPw / kThreads;  // outputs per thread (up and gate)
+template <typename T, bool kWriteState>
+__global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
+  constexpr int kPw = kS1Pw;
+  constexpr int kLpr = kS1Lpr;
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_wave_cnt[4];
-  __shared__ float s_wave_a[2][4];
+  __shared__ int s_wave_cnt[kS1Waves];
+  __shared__ float s_wave_a[2][kS1Waves];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -112,26 +124,26 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   // barrier is needed before the gather starts.
   const int row0 = split * a.rows_per_split;
   const int row1 = min(d, row0 + a.rows_per_split);
-  constexpr int kWaveSlots = 64 / kLpr;                    // rows in flight per wave load
-  constexpr int kBatchRows = kWaveSlots * kStage1Unroll;    // rows per gather batch
-  const int wchunk = (a.rows_per_split + 3) / 4;
+  constexpr int kWaveSlots = kS1WaveSlots;
+  constexpr int kBatchRows = kS1BatchRows;
+  const int wchunk = (a.rows_per_split + kS1Waves - 1) / kS1Waves;
   // the lists hold whole batches: positions past the last kept row up to the
   // batch end are zero-weight sentinels that read row 0
-  const int wcap = (wchunk + kS1ListBatch - 1) / kS1ListBatch * kS1ListBatch;
+  const int wcap = s1_wave_cap(a.rows_per_split);
   const int ucap = wcap / kWaveSlots;
   const int wr0 = min(row1, row0 + wave * wchunk);
   const int wr1 = min(row1, wr0 + wchunk);
   KeptA* ka = reinterpret_cast<KeptA*>(smem) + wave * wcap;
   // row byte offsets, transposed: position p at koff[(p % kWaveSlots) * ucap +
   // p / kWaveSlots], so the offsets a lane gathers in one batch are contiguous
-  uint32_t* koff = reinterpret_cast<uint32_t*>(reinterpret_cast<KeptA*>(smem) + 4 * wcap) + wave * wcap;
+  uint32_t* koff = reinterpret_cast<uint32_t*>(reinterpret_cast<KeptA*>(smem) + kS1Waves * wcap) + wave * wcap;
   constexpr float k2p24 = 16777216.0f;
   constexpr float k2p20 = 1048576.0f;
   int nkept = 0;
   float sum_up = 0.f, sum_gate = 0.f;
   // x and both scales of kCompactSteps 64-row steps are fetched before any is
-  // used (one memory round trip for a wave's 128 rows at 512 rows per split)
-  constexpr int kCompactSteps = 4;
+  // used (one memory round trip for a wave's share at 512 rows per split)
+  constexpr int kCompactSteps = 512 / (64 * kS1Waves);
   for (int base = wr0; base < wr1; base += 64 * kCompactSteps) {
     float xv[kCompactSteps], sc_up[kCompactSteps], sc_gate[kCompactSteps];
 #pragma unroll
@@ -185,27 +197,27 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     acc_u[e] = 0.f;
     acc_g[e] = 0.f;
   }
-  // One batch covers kBatchRows = 128 rows (kPw 128), a wave's whole share
-  // at 512 rows per split, so every wave makes a single round trip.  The
+  // One batch covers kBatchRows rows, a wave's whole share at 512 rows per
+  // split, so every wave makes a single round trip.  The
   // batch's offsets come from LDS as 16-byte vectors, then all its loads are
   // issued (sentinel slots read row 0); a = x_i * scale_i of the next row is
   // read from LDS while the current row is added, and steps with no kept row
   // in any slot are skipped.
   for (int rb = 0; rb < nkept; rb += kBatchRows) {  // wave-uniform
     const uint32_t* ko = koff + wslot * ucap + rb / kWaveSlots;
-    uint32_t off[kStage1Unroll];
+    uint32_t off[kS1Unroll];
 #pragma unroll
-    for (int u = 0; u < kStage1Unroll; ++u) off[u] = ko[u];
-    uint4 w[kStage1Unroll];
+    for (int u = 0; u < kS1Unroll; ++u) off[u] = ko[u];
+    uint4 w[kS1Unroll];
 #pragma unroll
-    for (int u = 0; u < kStage1Unroll; ++u) w[u] = ldg16(qbase + (off[u] + coff));
+    for (int u = 0; u < kS1Unroll; ++u) w[u] = ldg16(qbase + (off[u] + coff));
     __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
     const KeptA* kb = ka + rb + wslot;
     KeptA cur = kb[0];
 #pragma unroll
-    for (int u = 0; u < kStage1Unroll; ++u) {
+    for (int u = 0; u < kS1Unroll; ++u) {
       KeptA nxt = cur;
-      if (u + 1 < kStage1Unroll) nxt = kb[(u + 1) * kWaveSlots];
+      if (u + 1 < kS1Unroll) nxt = kb[(u + 1) * kWaveSlots];
       if (rb + u * kWaveSlots < nkept) {
         acc_dword(acc_u + 0, w[u].x, cur.u24, cur.u20);
         acc_dword(acc_u + 8, w[u].y, cur.u24, cur.u20);
@@ -225,29 +237,30 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
     red[(16 + e) * kRedStride + tid] = acc_g[e];
   }
   __syncthreads();
-  float v[kNout];
-  size_t col[kNout];
-  int mm[kNout];
-#pragma unroll
-  for (int k = 0; k < kNout; ++k) {
-    const int o = tid + k * kThreads;
-    const int m = o / kPw;  // 0 = up, 1 = gate
+  // outputs: threads 0 .. 2 kPw - 1 (up, then gate, of the panel's columns)
+  const bool has_out = tid < 2 * kPw;
+  const int o = has_out ? tid : 0;
+  const int mo = o / kPw;  // 0 = up, 1 = gate
+  const size_t col = static_cast<size_t>(panel) * kPw + (o % kPw);
+  if (has_out) {
     const int c = o % kPw;
     const int ch = c >> 4;
     const int e = c & 15;
     float t = 0.f;
 #pragma unroll 8
-    for (int sl = 0; sl < kSlots; ++sl) t += red[(m * 16 + e) * kRedStride + sl * kLpr + ch];
-    const float suma = (s_wave_a[m][0] + s_wave_a[m][1]) + (s_wave_a[m][2] + s_wave_a[m][3]);
-    v[k] = fmaf(-8.0f, suma, t);
-    col[k] = static_cast<size_t>(panel) * kPw + c;
-    mm[k] = m;
-    __hip_atomic_store(&partial[(static_cast<size_t>(split) * 2 + m) * f + col[k]], v[k],
+    for (int sl = 0; sl < kS1RedSlots; ++sl) t += red[(mo * 16 + e) * kRedStride + sl * kLpr + ch];
+    float suma = 0.f;
+#pragma unroll
+    for (int w = 0; w < kS1Waves; ++w) suma += s_wave_a[mo][w];
+    __hip_atomic_store(&partial[(static_cast<size_t>(split) * 2 + mo) * f + col], fmaf(-8.0f, suma, t),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (panel == 0 && tid == 0)
-    __hip_atomic_store(&kcount[split], s_wave_cnt[0] + s_wave_cnt[1] + s_wave_cnt[2] + s_wave_cnt[3],
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (panel == 0 && tid == 0) {
+    int kc = 0;
+#pragma unroll
+    for (int w = 0; w < kS1Waves; ++w) kc += s_wave_cnt[w];
+    __hip_atomic_store(&kcount[split], kc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // ---- last block of this panel: fixed-order sum of the splits, activation, mask
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are complete
@@ -263,25 +276,24 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Args a) {
   // split loads go out in groups of 8 so they travel together; the sums keep
   // the fixed split order
   float* sv = red;  // every thread finished reading red before the ticket barrier
-#pragma unroll
-  for (int k = 0; k < kNout; ++k) {
+  if (has_out) {
     float tot = 0.f;
     for (int k0 = 0; k0 < a.splits; k0 += 8) {
       float pv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int kk = min(k0 + u, a.splits - 1);
-        pv[u] = __hip_atomic_load(&partial[(static_cast<size_t>(kk) * 2 + mm[k]) * f + col[k]],
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pv[u] = __hip_atomic_load(&partial[(static_cast<size_t>(kk) * 2 + mo) * f + col], __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (k0 + u < a.splits) tot += pv[u];
     }
-    sv[tid + k * kThreads] = tot;
+    sv[tid] = tot;
   }
   __syncthreads();
-  for (int c = tid; c < kPw; c += kThreads) {  // wave-uniform trip count
+  for (int c = tid; c < kPw; c += kS1Threads) {  // wave-uniform trip count
     const float uu = sv[c];
     const float gg = sv[kPw + c];
     const float st = uu * gate_act(gg, a.act);
@@ -313,27 +325,21 @@ hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_
                          hipStream_t s) {
   if (a.proxy_kind == PROX_PROXY_W16) return launch_stage1_w16(a, batch, write_state, s);
   const dim3 grid(static_cast<unsigned>(a.n_panels * a.splits), static_cast<unsigned>(batch));
-  const size_t wcap = static_cast<size_t>(((a.rows_per_split + 3) / 4 + kS1ListBatch - 1) / kS1ListBatch) * kS1ListBatch;
-  const size_t kept_bytes = 4 * wcap * (sizeof(KeptA) + sizeof(uint32_t));
+  const size_t kept_bytes =
+      static_cast<size_t>(kS1Waves) * s1_wave_cap(a.rows_per_split) * (sizeof(KeptA) + sizeof(uint32_t));
   const size_t red_bytes = static_cast<size_t>(32) * kRedStride * sizeof(float);
   const size_t smem = kept_bytes > red_bytes ? kept_bytes : red_bytes;
-#define PROX_S1_LAUNCH(TAG, WS, PW) \
-  hipLaunchKernelGGL((stage1_kernel<TAG, WS, PW>), grid, dim3(kThreads), smem, s, a)
-  const bool wide = a.panel == 256;
   if (wdtype == PROX_BF16) {
-    if (write_state) {
-      if (wide) PROX_S1_LAUNCH(Bf16Tag, true, 256); else PROX_S1_LAUNCH(Bf16Tag, true, 128);
-    } else {
-      if (wide) PROX_S1_LAUNCH(Bf16Tag, false, 256); else PROX_S1_LAUNCH(Bf16Tag, false, 128);
-    }
+    if (write_state)
+      hipLaunchKernelGGL((stage1_kernel<Bf16Tag, true>), grid, dim3(kS1Threads), smem, s, a);
+    else
+      hipLaunchKernelGGL((stage1_kernel<Bf16Tag, false>), grid, dim3(kS1Threads), smem, s, a);
   } else {
-    if (write_state) {
-      if (wide) PROX_S1_LAUNCH(F32Tag, true, 256); else PROX_S1_LAUNCH(F32Tag, true, 128);
-    } else {
-      if (wide) PROX_S1_LAUNCH(F32Tag, false, 256); else PROX_S1_LAUNCH(F32Tag, false, 128);
-    }
+    if (write_state)
+      hipLaunchKernelGGL((stage1_kernel<F32Tag, true>), grid, dim3(kS1Threads), smem, s, a);
+    else
+      hipLaunchKernelGGL((stage1_kernel<F32Tag, false>), grid, dim3(kS1Threads), smem, s, a);
   }
-#undef PROX_S1_LAUNCH
   return hipGetLastError();
 }
 
