@@ -12,9 +12,13 @@
 //
 // gfx950 design:
 //   * grid = panels x K-splits (split-major, as the batch-1 kernel), one
-//     512-thread block per (panel of 128 output columns, range of input rows),
-//     all tokens of the group in the block; each of the 8 waves owns one
-//     16-column chunk of the panel (up and gate).
+//     256-thread block per (panel of 128 output columns, range of input rows),
+//     all tokens of the group in the block; each of the 4 waves owns two
+//     16-column chunks of the panel (up and gate).  Three blocks fit on a CU
+//     (LDS ~52 KB, at most 168 VGPRs), so the 768 blocks of a Qwen3-8B-shaped
+//     layer are all resident at once: a block's chain of memory round trips
+//     (x, gather, partials, ticket) is paid once, not once per round of
+//     blocks.
 //   * contraction on the matrix cores, v_mfma_f32_16x16x32_f16: the 16 rows
 //     of the A operand are (token, part) pairs, the token's weights
 //     a = x_b,i * scale_i split into a high and a low f16 part (hi + lo
@@ -38,29 +42,35 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2_t;
 
-constexpr int kS1bThreads = 512;                 // 8 waves, one 16-column chunk each
+constexpr int kS1bThreads = 256;                 // 4 waves, two 16-column chunks each
 constexpr int kS1bWaves = kS1bThreads / 64;
-constexpr int kChunkRows = 512;                  // input rows per pass (64 per wave)
+constexpr int kChunkRows = 512;                  // input rows per pass (two per thread)
+constexpr int kRowGroups = kChunkRows / 64;      // 64-row groups of a pass, one wave's rows each
+constexpr int kWaveChunks = (128 / 16) / kS1bWaves;  // 16-column chunks per wave
 constexpr int kTileRows = 64;                    // rows per pair of MFMA K-steps
 constexpr int kTiles = kChunkRows / kTileRows;   // 8
 constexpr int kPhaseRows = 128;                  // rows staged in LDS at a time
 constexpr int kPw = 128;                         // panel width (output columns)
-constexpr int kRowsPerLoad = kS1bThreads / 8;    // 64 rows per load round (8 threads x 16 B per row)
-constexpr int kLoads = kChunkRows / kRowsPerLoad;  // 8 loads of 16 B per thread per pass
-constexpr int kLoadsPerPhase = kPhaseRows / kRowsPerLoad;  // 2
+constexpr int kRowsPerLoad = kS1bThreads / 8;    // 32 rows per load round (8 threads x 16 B per row)
+constexpr int kLoads = kChunkRows / kRowsPerLoad;  // 16 loads of 16 B per thread per pass
+constexpr int kLoadsPerPhase = kPhaseRows / kRowsPerLoad;  // 4
 
 // LDS: the A operands of one pass [mat][tile][half][k-group][m][8], the staged
 // code rows of one phase, the pass's union-row offsets, per-wave statistics.
 struct S1BShared {
   _Float16 A[2][kTiles][2][4][16][8];
   uint8_t B[kPhaseRows * kPw];
-  uint32_t uoff[kChunkRows];
-  float wmax[kS1bWaves][kBatchMax];
+  uint32_t uoff[kChunkRows];  // union-row byte offsets, transposed (uoff_pos)
+  float wmax[kRowGroups][kBatchMax];
   int wkept[kS1bWaves][kBatchMax];
-  int wunion[kS1bWaves];
+  int wunion[kRowGroups];
   int sexp[kBatchMax];
   int last;
 };
+
+// Union slot p's offset lives at uoff[uoff_pos(p)]: the kLoads slots one
+// thread gathers (p = kRowsPerLoad u + tid / 8) are contiguous.
+__device__ __forceinline__ int uoff_pos(int p) { return (p & (kRowsPerLoad - 1)) * kLoads + p / kRowsPerLoad; }
 
 // Eight stored nibbles (code + 8) of one column, rows in the order
 // 0, 4, 1, 5, 2, 6, 3, 7 of the dword, as signed f16 codes: a nibble n put
@@ -96,7 +106,7 @@ __device__ __forceinline__ int scale_exponent(float m) {
 }
 
 template <typename T, bool kWriteState>
-__global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))) void stage1_batch_kernel(Stage1Args a) {
+__global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(3))) void stage1_batch_kernel(Stage1Args a) {
   __shared__ __align__(16) S1BShared sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,9 +122,9 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))
   int kept[kBatchMax];  // per-wave counts of kept rows per token (wave-uniform)
 #pragma unroll
   for (int t = 0; t < kBatchMax; ++t) kept[t] = 0;
-  float acc[2][2];  // unscaled sums of this block: [matrix][token 2g + i]
+  float acc[kWaveChunks][2][2];  // unscaled sums of this block: [chunk][matrix][token 2g + i]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) (&acc[0][0])[i] = 0.f;
+  for (int i = 0; i < 4 * kWaveChunks; ++i) (&acc[0][0][0])[i] = 0.f;
 
   const int g = lane >> 4;     // MFMA k-group
   const int mrow = lane & 15;  // A row: token mrow/2, part mrow%2
@@ -131,32 +141,42 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))
       const u32x4_t z = {0u, 0u, 0u, 0u};
       for (int i = tid; i < n16; i += kS1bThreads) az[i] = z;
     }
-    // ---- input masks of the pass: wave w takes rows c0 + 64w + lane
-    const int i = c0 + 64 * wave + lane;
-    const int ii = min(i, c1 - 1);
-    float xv[kBatchMax];
-    const float sc_u = a.proxy_scale[ii];
-    const float sc_g = a.proxy_scale[d + ii];
+    // ---- input masks of the pass: row group h * kS1bWaves + wave holds rows
+    // c0 + 64 (h * kS1bWaves + wave) + lane, h = 0, 1
+    int iv[2];
+    float xv[2][kBatchMax], sc_u[2], sc_g[2];
 #pragma unroll
-    for (int t = 0; t < kBatchMax; ++t)
-      xv[t] = load_elem<T>(a.x, static_cast<size_t>(min(t, nt - 1)) * d + ii);
+    for (int h = 0; h < 2; ++h) {
+      iv[h] = c0 + 64 * (h * kS1bWaves + wave) + lane;
+      const int ii = min(iv[h], c1 - 1);
+      sc_u[h] = a.proxy_scale[ii];
+      sc_g[h] = a.proxy_scale[d + ii];
+#pragma unroll
+      for (int t = 0; t < kBatchMax; ++t)
+        xv[h][t] = load_elem<T>(a.x, static_cast<size_t>(min(t, nt - 1)) * d + ii);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t keep = 0u;
-    float lmax[kBatchMax];
+    uint32_t keep[2];
+    uint64_t bal[2];
 #pragma unroll
-    for (int t = 0; t < kBatchMax; ++t) {
-      const bool kp = t < nt && i < c1 && fabsf(xv[t]) >= a.tau_x;
-      keep |= kp ? (1u << t) : 0u;
-      lmax[t] = kp ? fmaxf(fabsf(xv[t] * sc_u), fabsf(xv[t] * sc_g)) : 0.f;
-    }
-    const uint64_t bal = __ballot(keep != 0u);
+    for (int h = 0; h < 2; ++h) {
+      keep[h] = 0u;
+      float lmax[kBatchMax];
 #pragma unroll
-    for (int t = 0; t < kBatchMax; ++t) {
-      const float v = wave_max_nonneg(lmax[t]);
-      if (lane == 0) sh.wmax[wave][t] = v;
-      kept[t] += __popcll(__ballot((keep >> t) & 1u));
+      for (int t = 0; t < kBatchMax; ++t) {
+        const bool kp = t < nt && iv[h] < c1 && fabsf(xv[h][t]) >= a.tau_x;
+        keep[h] |= kp ? (1u << t) : 0u;
+        lmax[t] = kp ? fmaxf(fabsf(xv[h][t] * sc_u[h]), fabsf(xv[h][t] * sc_g[h])) : 0.f;
+      }
+      bal[h] = __ballot(keep[h] != 0u);
+#pragma unroll
+      for (int t = 0; t < kBatchMax; ++t) {
+        const float v = wave_max_nonneg(lmax[t]);
+        if (lane == 0) sh.wmax[h * kS1bWaves + wave][t] = v;
+        kept[t] += __popcll(__ballot((keep[h] >> t) & 1u));
+      }
+      if (lane == 0) sh.wunion[h * kS1bWaves + wave] = __popcll(bal[h]);
     }
-    if (lane == 0) sh.wunion[wave] = __popcll(bal);
     __syncthreads();
     int sexp[kBatchMax];
     float scale[kBatchMax];
@@ -164,63 +184,84 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))
     for (int t = 0; t < kBatchMax; ++t) {
       float m = 0.f;
 #pragma unroll
-      for (int w = 0; w < kS1bWaves; ++w) m = fmaxf(m, sh.wmax[w][t]);
+      for (int w = 0; w < kRowGroups; ++w) m = fmaxf(m, sh.wmax[w][t]);
       sexp[t] = scale_exponent(m);
       scale[t] = ldexpf(1.0f, 15 - sexp[t]);
     }
-    int wbase = 0, nu = 0;
+    int nu = 0;
 #pragma unroll
-    for (int w = 0; w < kS1bWaves; ++w) {
-      wbase += w < wave ? sh.wunion[w] : 0;
-      nu += sh.wunion[w];
+    for (int w = 0; w < kRowGroups; ++w) nu += sh.wunion[w];
+    // ---- union slots (ascending rows); slots past the union read row 0
+    int slot[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rg = h * kS1bWaves + wave;
+      int wbase = 0;
+#pragma unroll
+      for (int w = 0; w < kRowGroups; ++w) wbase += w < rg ? sh.wunion[w] : 0;
+      slot[h] = wbase + __popcll(bal[h] & ((1ull << lane) - 1ull));
+      if (keep[h] != 0u)
+        sh.uoff[uoff_pos(slot[h])] = static_cast<uint32_t>(iv[h]) * static_cast<uint32_t>(a.proxy_stride);
+      const int pz = h * kS1bThreads + tid;
+      if (pz >= nu) sh.uoff[uoff_pos(pz)] = 0u;
     }
-    // ---- union slots (ascending rows)
-    const int slot = wbase + __popcll(bal & ((1ull << lane) - 1ull));
-    if (keep != 0u) sh.uoff[slot] = static_cast<uint32_t>(i) * static_cast<uint32_t>(a.proxy_stride);
     if (tid < kBatchMax) sh.sexp[tid] = sexp[tid];
     __syncthreads();
 
-    // ---- gather the union rows' panel slices (thread -> row tid/8 + 64u,
+    // ---- gather the union rows' panel slices (thread -> row tid/8 + 32u,
     // 16-B chunk tid%8), issued before the A operands are written so the two
-    // overlap
+    // overlap.  All loads are issued unconditionally (slots past the union
+    // re-read row 0, which the phases below never use), so each phase waits
+    // only for its own loads.
     const int ntile = (nu + kTileRows - 1) / kTileRows;
     const int rows_pad = ntile * kTileRows;
     const uint8_t* pbase = a.proxy_q + static_cast<size_t>(panel) * kPw + chunk * 16;
-    u32x4_t wld[kLoads];
+    uint32_t offs[kLoads];
+    {
+      const u32x4_t* uo = reinterpret_cast<const u32x4_t*>(&sh.uoff[(tid >> 3) * kLoads]);
 #pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      wld[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (u * kRowsPerLoad < rows_pad) {  // block-uniform (rows_pad is a multiple of 64)
-        const int rs = u * kRowsPerLoad + (tid >> 3);
-        wld[u] = *reinterpret_cast<const u32x4_t*>(pbase + sh.uoff[min(rs, nu - 1)]);
+      for (int k = 0; k < kLoads / 4; ++k) {
+        const u32x4_t o = uo[k];
+        offs[4 * k] = o.x;
+        offs[4 * k + 1] = o.y;
+        offs[4 * k + 2] = o.z;
+        offs[4 * k + 3] = o.w;
       }
     }
+    u32x4_t wld[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) wld[u] = *reinterpret_cast<const u32x4_t*>(pbase + offs[u]);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- A operands: (token, hi/lo) rows in the slot order of the staged rows
-    if (keep != 0u) {
-      const int tile = slot / kTileRows;
-      const int gg = (slot >> 4) & 3;
-      const int h = (slot >> 3) & 1;
-      const int r = slot & 7;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (keep[h] == 0u) continue;
+      const int sl = slot[h];
+      const int tile = sl / kTileRows;
+      const int gg = (sl >> 4) & 3;
+      const int hh = (sl >> 3) & 1;
+      const int r = sl & 7;
       const int e = 2 * (r & 3) + (r >> 2);
       const float rs = (r & 1) ? kInv16 : 1.0f;  // odd rows pair with high nibbles
 #pragma unroll
       for (int t = 0; t < kBatchMax; ++t) {
-        if (!((keep >> t) & 1u)) continue;
+        if (!((keep[h] >> t) & 1u)) continue;
 #pragma unroll
         for (int mat = 0; mat < 2; ++mat) {
-          const float v = xv[t] * (mat == 0 ? sc_u : sc_g) * scale[t] * rs;
+          const float v = xv[h][t] * (mat == 0 ? sc_u[h] : sc_g[h]) * scale[t] * rs;
           const _Float16 hi = static_cast<_Float16>(v);
           const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
-          sh.A[mat][tile][h][gg][2 * t][e] = hi;
-          sh.A[mat][tile][h][gg][2 * t + 1][e] = lo;
+          sh.A[mat][tile][hh][gg][2 * t][e] = hi;
+          sh.A[mat][tile][hh][gg][2 * t + 1][e] = lo;
         }
       }
     }
     __syncthreads();
 
-    f32x4_t C[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    f32x4_t C[kWaveChunks][2];
+#pragma unroll
+    for (int j = 0; j < kWaveChunks; ++j) C[j][0] = C[j][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < kChunkRows / kPhaseRows; ++q) {
       if (q * kPhaseRows >= rows_pad) break;  // block-uniform
@@ -243,11 +284,15 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))
         for (int hf = 0; hf < 2; ++hf) {
           const f16x8_t a0 = *reinterpret_cast<const f16x8_t*>(&sh.A[hf][tile][0][g][mrow][0]);
           const f16x8_t a1 = *reinterpret_cast<const f16x8_t*>(&sh.A[hf][tile][1][g][mrow][0]);
-          const int off = r * kPw + 16 * (wave ^ (r & 7)) + 8 * (hf ^ ((r >> 3) & 1));
-          const i32x2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2_t*)((__attribute__((address_space(3))) uint8_t*)(sh.B) + off));
-          C[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, codes_to_f16(static_cast<uint32_t>(v[0])), C[hf], 0, 0, 0);
-          C[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, codes_to_f16(static_cast<uint32_t>(v[1])), C[hf], 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < kWaveChunks; ++j) {
+            const int cw = wave + kS1bWaves * j;
+            const int off = r * kPw + 16 * (cw ^ (r & 7)) + 8 * (hf ^ ((r >> 3) & 1));
+            const i32x2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2_t*)((__attribute__((address_space(3))) uint8_t*)(sh.B) + off));
+            C[j][hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, codes_to_f16(static_cast<uint32_t>(v[0])), C[j][hf], 0, 0, 0);
+            C[j][hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, codes_to_f16(static_cast<uint32_t>(v[1])), C[j][hf], 0, 0, 0);
+          }
         }
       }
       __syncthreads();  // the staging buffer is rewritten by the next phase
@@ -257,10 +302,12 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))
     const int e0 = sh.sexp[2 * g];
     const int e1 = sh.sexp[2 * g + 1];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      acc[hf][0] += ldexpf(C[hf][0] + C[hf][1], e0 - 15);
-      acc[hf][1] += ldexpf(C[hf][2] + C[hf][3], e1 - 15);
-    }
+    for (int j = 0; j < kWaveChunks; ++j)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        acc[j][hf][0] += ldexpf(C[j][hf][0] + C[j][hf][1], e0 - 15);
+        acc[j][hf][1] += ldexpf(C[j][hf][2] + C[j][hf][3], e1 - 15);
+      }
     __syncthreads();  // sexp, wmax and A are rewritten by the next pass
   }
 
@@ -271,18 +318,22 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
   __syncthreads();
 
-  // ---- partials: lane (g, n) holds tokens 2g, 2g+1 of column n of the wave's chunk
+  // ---- partials: lane (g, n) holds tokens 2g, 2g+1 of column n of each of
+  // the wave's chunks
   const int n = lane & 15;
-  const int col = panel * kPw + wave * 16 + n;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int t = 2 * g + tt;
     if (t >= nt) continue;
     float* partial = reinterpret_cast<float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_partial);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      __hip_atomic_store(&partial[(static_cast<size_t>(split) * 2 + hf) * f + col], acc[hf][tt], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = 0; j < kWaveChunks; ++j) {
+      const int col = panel * kPw + (wave + kS1bWaves * j) * 16 + n;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        __hip_atomic_store(&partial[(static_cast<size_t>(split) * 2 + hf) * f + col], acc[j][hf][tt],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (panel == 0 && tid < nt) {
     int* kcount = reinterpret_cast<int*>(a.ws + static_cast<size_t>(tid) * a.tok_bytes + a.off_kcount);
@@ -305,20 +356,22 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))
   __syncthreads();
   if (!sh.last) return;
 
-  // each half of the block loads four tokens' split partials in one go (fixed
-  // split order in the sums); then wave w forms token w's state and mask bits
+  // thread o loads output o (up, then gate, of the panel's columns) of every
+  // token for 8 splits at a time (fixed split order in the sums); then wave w
+  // forms the state and mask bits of tokens w and w + 4
   float* sv = reinterpret_cast<float*>(sh.B);  // [token][2 * kPw]
-  const int o = tid & 255;
+  const int o = tid;
   const int mm = o / kPw;  // 0 = up, 1 = gate
   const size_t ocol = static_cast<size_t>(panel) * kPw + (o % kPw);
-  const int tb = 4 * (tid >> 8);
-  float tot[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.splits; k0 += 8) {
-    float pv[4][8];
+  float tot[kBatchMax];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < kBatchMax; ++t) tot[t] = 0.f;
+  for (int k0 = 0; k0 < a.splits; k0 += 8) {
+    float pv[kBatchMax][8];
+#pragma unroll
+    for (int t = 0; t < kBatchMax; ++t) {
       const float* partial = reinterpret_cast<const float*>(
-          a.ws + static_cast<size_t>(min(tb + t, nt - 1)) * a.tok_bytes + a.off_partial);
+          a.ws + static_cast<size_t>(min(t, nt - 1)) * a.tok_bytes + a.off_partial);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int kk = min(k0 + u, a.splits - 1);
@@ -327,17 +380,19 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(4))
       }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < kBatchMax; ++t)
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (k0 + u < a.splits) tot[t] += pv[t][u];
   }
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    if (tb + t < nt) sv[(tb + t) * 2 * kPw + o] = tot[t];
+  for (int t = 0; t < kBatchMax; ++t)
+    if (t < nt) sv[t * 2 * kPw + o] = tot[t];
   __syncthreads();
-  if (wave < nt) {
-    const int t = wave;
+#pragma unroll
+  for (int tw = 0; tw < kBatchMax / kS1bWaves; ++tw) {
+    const int t = wave + kS1bWaves * tw;
+    if (t >= nt) continue;  // wave-uniform
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_bitmap);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
