@@ -9,11 +9,12 @@
 // for a token that does not keep j, so each y_b sums exactly its own J_b.
 //
 // gfx950 design:
-//   * upgate_batch_kernel: every block owns 16 consecutive channels and reads
-//     the union channels among them (one bitmap word per token); it writes
-//     their entries of the union list and of the per-token index lists at
-//     offsets summed from the earlier bitmap words while its first weight
-//     tile is in flight.  Two waves per 8 channels split d in halves.
+//   * upgate_batch_kernel: every block turns the tokens' Stage-1 bitmaps into
+//     the union channel list and the per-token index lists (block scans of
+//     the popcounts) for its slice of 16 union ordinals; the slice is filled
+//     by whole waves, 32 lanes on the bits of one word at a time (a single
+//     lane walking a word's bits and tokens took longer than the weight
+//     stream).  Two waves per 8 channels split d in halves.
 //     v_mfma_f32_16x16x32_bf16: A rows are the tokens' x (rows 8..15 zero),
 //     B columns are the up rows (0..7) and the gate rows (8..15) of the 8
 //     channels, read from K-tiles of W^T staged in LDS (the contraction runs
@@ -60,16 +61,117 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 // ---------------------------------------------------------------------------
 // up/gate
 // ---------------------------------------------------------------------------
-// Each up/gate block owns a fixed range of 16 channels (a half bitmap word)
-// and computes the union channels in it, so its weight loads wait for one
-// round trip of bitmap words only.  The union list (ulist, U at ulist[f]) and
-// every token's index list need the counts of all earlier channels: the
-// block's own share of the bitmap words before its range is loaded in the same
-// round trip, and the block-wide sums are formed while the first weight tile
-// is in flight.  kPasses >= d_ff / (32 * kThreads) words per thread.
-template <int kPasses>
+// The union of a group's channel masks, as every up/gate block needs it: the
+// union ordinals [u0, u0 + kSlice) of this block go to s_ch (channel) and s_tb
+// (bit t set when token t keeps the channel) and to ulist; each token's index
+// list receives the entries of those channels; block 0 publishes U (at
+// ulist[f]) and every token's k_s.  Returns U.  The bitmap is read in passes
+// of one word per thread per token; a block scan of the 1 + nt popcounts
+// gives every word its union and per-token prefixes.  The slice is then
+// filled with all lanes of a wave on the 32 bits of one overlapping word at a
+// time (its data broadcast with readlane), not by the word's own thread.
+// The first pass's words come preloaded (union_words), so that a caller can
+// issue other loads behind them before the block's first barrier.
+template <int kNT>
+__device__ __forceinline__ void union_words(const UpGateBatchArgs& a, int pass, uint32_t (&tw)[kBatchMax]) {
+  const int nw = a.f / 32;
+  const int w = min(pass * kNT + static_cast<int>(threadIdx.x), nw - 1);
+#pragma unroll
+  for (int t = 0; t < kBatchMax; ++t)
+    tw[t] = reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(min(t, a.nt - 1)) * a.tok_bytes +
+                                              a.off_bitmap)[w];
+}
+
+template <int kNT, int kSlice>
+__device__ __forceinline__ int union_slice(const UpGateBatchArgs& a, int u0, int (&s_scan)[2][kNT / 64][1 + kBatchMax],
+                                           int* s_ch, uint32_t* s_tb, uint32_t (&tw)[kBatchMax]) {
+  constexpr int kW = kNT / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int f = a.f;
+  const int nt = a.nt;
+  const int nw = f / 32;
+  const int npass = (nw + kNT - 1) / kNT;
+  int* ulist = reinterpret_cast<int*>(a.ws + a.off_ulist);
+  int base[1 + kBatchMax];
+#pragma unroll
+  for (int q = 0; q <= kBatchMax; ++q) base[q] = 0;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int w = pass * kNT + tid;
+    if (pass > 0) union_words<kNT>(a, pass, tw);
+    uint32_t uw = 0u;
+    int cnt[1 + kBatchMax];
+#pragma unroll
+    for (int t = 0; t < kBatchMax; ++t) {
+      tw[t] = (t < nt && w < nw) ? tw[t] : 0u;
+      uw |= tw[t];
+      cnt[1 + t] = __popc(tw[t]);
+    }
+    cnt[0] = __popc(uw);
+    int inc[1 + kBatchMax];
+#pragma unroll
+    for (int q = 0; q <= kBatchMax; ++q) inc[q] = wave_inclusive_scan_int(cnt[q]);
+    if (lane == 63) {
+#pragma unroll
+      for (int q = 0; q <= kBatchMax; ++q) s_scan[pass & 1][wave][q] = inc[q];
+    }
+    __syncthreads();
+    int excl[1 + kBatchMax];
+#pragma unroll
+    for (int q = 0; q <= kBatchMax; ++q) {
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int v = 0; v < kW; ++v) {
+        const int c = s_scan[pass & 1][v][q];
+        pre += v < wave ? c : 0;
+        tot += c;
+      }
+      excl[q] = base[q] + pre + inc[q] - cnt[q];
+      base[q] += tot;
+    }
+    // words of this wave that hold ordinals of the slice, one at a time
+    uint64_t ovm = __ballot(cnt[0] > 0 && excl[0] < u0 + kSlice && excl[0] + cnt[0] > u0);
+    while (ovm) {  // wave-uniform
+      const int src = static_cast<int>(__builtin_ctzll(ovm));
+      ovm &= ovm - 1ull;
+      const uint32_t su = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(uw), src));
+      const int se = __builtin_amdgcn_readlane(excl[0], src);
+      uint32_t st[kBatchMax];
+      int sx[kBatchMax];
+#pragma unroll
+      for (int t = 0; t < kBatchMax; ++t) {
+        st[t] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw[t]), src));
+        sx[t] = __builtin_amdgcn_readlane(excl[1 + t], src);
+      }
+      const int bit = lane & 31;
+      const uint32_t below = (1u << bit) - 1u;
+      const int o = se + __popc(su & below);
+      if (lane < 32 && ((su >> bit) & 1u) && o >= u0 && o < u0 + kSlice) {
+        const int j = (pass * kNT + wave * 64 + src) * 32 + bit;
+        uint32_t tb = 0u;
+#pragma unroll
+        for (int t = 0; t < kBatchMax; ++t) {
+          if ((st[t] >> bit) & 1u) {
+            tb |= 1u << t;
+            a.mask_idx[static_cast<size_t>(t) * f + sx[t] + __popc(st[t] & below)] = j;
+          }
+        }
+        s_ch[o - u0] = j;
+        s_tb[o - u0] = tb;
+        ulist[o] = j;
+      }
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    ulist[f] = base[0];
+    for (int t = 0; t < nt; ++t) a.mask_count[t] = base[1 + t];
+  }
+  return base[0];
+}
+
 __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs a) {
-  __shared__ int s_cnt[kThreads / 64][1 + kBatchMax];
+  __shared__ int s_scan[2][kThreads / 64][1 + kBatchMax];
   __shared__ int s_ch[kUgbChannels];
   __shared__ uint32_t s_tb[kUgbChannels];
   __shared__ float s_red[2][64][4];
@@ -82,42 +184,13 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
   const int d = a.d;
   const int nt = a.nt;
 
-  const int f = a.f;
-  const int nw = f / 32;
-  const int c0 = static_cast<int>(blockIdx.x) * kUgbChannels;  // channels [c0, c0 + 16)
-  const int w0 = c0 / 32;
-  const int hsh = c0 & 16;  // bit offset of the range in word w0
-  // ---- bitmap words, all in flight together: the range's word of every
-  // token and this thread's words before w0
-  uint32_t own[kBatchMax];
-  uint32_t pw[kPasses][kBatchMax];
-#pragma unroll
-  for (int t = 0; t < kBatchMax; ++t) {
-    const uint32_t* bm =
-        reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(min(t, nt - 1)) * a.tok_bytes + a.off_bitmap);
-    own[t] = bm[w0];
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) pw[p][t] = bm[min(p * kThreads + tid, nw - 1)];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // ---- the range's union channels, ascending: s_ch (channel), s_tb (bit t
-  // set when token t keeps it)
-  uint32_t mine[kBatchMax];  // the range's 16 bits per token
-  uint32_t u16 = 0u;
-#pragma unroll
-  for (int t = 0; t < kBatchMax; ++t) {
-    mine[t] = t < nt ? (own[t] >> hsh) & 0xFFFFu : 0u;
-    u16 |= mine[t];
-  }
-  const int nloc = __popc(u16);
-  if (tid < kUgbChannels && ((u16 >> tid) & 1u)) {
-    uint32_t tb = 0u;
-#pragma unroll
-    for (int t = 0; t < kBatchMax; ++t) tb |= ((mine[t] >> tid) & 1u) << t;
-    const int pos = __popc(u16 & ((1u << tid) - 1u));
-    s_ch[pos] = c0 + tid;
-    s_tb[pos] = tb;
-  }
+  const int u0 = static_cast<int>(blockIdx.x) * kUgbChannels;
+  uint32_t tw[kBatchMax];
+  union_words<kThreads>(a, 0, tw);
+  const int U = union_slice<kThreads, kUgbChannels>(a, u0, s_scan, s_ch, s_tb, tw);
+  if (u0 >= U) return;  // block-uniform
+  const int u1 = min(U, u0 + kUgbChannels);
+  const int nloc = u1 - u0;
   __syncthreads();
 
   // ---- MFMA: wave -> (channel half ch = wave & 1, K half kh = wave >> 1)
@@ -126,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
   const int n = lane & 15;
   const int g = lane >> 4;
   const int slot = chh * 8 + (n & 7);
-  const int j = s_ch[max(0, min(slot, nloc - 1))];
+  const int j = s_ch[min(slot, nloc - 1)];
   typedef uint16_t S;
   // K-tiles of 512 elements are staged in LDS: each wave load instruction
   // reads one contiguous 1 KB row segment (the DRAM-friendly pattern), and
@@ -143,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
   for (int q = 0; q < kUgbRowsPerThread; ++q) {
     const int r = (tid >> 6) + 4 * q;
     const int sl = 8 * (r >> 4) + (r & 7);
-    wsrc[q] = W + (static_cast<size_t>(s_ch[max(0, min(sl, nloc - 1))]) * 2 + ((r >> 3) & 1)) * d;
+    wsrc[q] = W + (static_cast<size_t>(s_ch[min(sl, nloc - 1)]) * 2 + ((r >> 3) & 1)) * d;
   }
   const int xt = tid >> 5;  // token row of this thread's x units
   const S* xsrc = X + static_cast<size_t>(min(xt, nt - 1)) * d;
@@ -168,72 +241,7 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
       xv[q] = (xon && k0 + xu * 8 < d) ? *reinterpret_cast<const u32x4_t*>(xsrc + k0 + xu * 8) : z;
     }
   };
-  if (nloc > 0) load_tile(0);
-
-  // ---- list offsets: union and per-token counts of the channels before c0
-  // (block sums of the words before w0, plus the low half of w0)
-  {
-    int cnt[1 + kBatchMax];
-#pragma unroll
-    for (int q = 0; q <= kBatchMax; ++q) cnt[q] = 0;
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const bool on = p * kThreads + tid < w0;
-      uint32_t uw = 0u;
-#pragma unroll
-      for (int t = 0; t < kBatchMax; ++t) {
-        const uint32_t v = (on && t < nt) ? pw[p][t] : 0u;
-        uw |= v;
-        cnt[1 + t] += __popc(v);
-      }
-      cnt[0] += __popc(uw);
-    }
-    if (tid == 0 && hsh != 0) {
-      uint32_t uw = 0u;
-#pragma unroll
-      for (int t = 0; t < kBatchMax; ++t) {
-        const uint32_t v = t < nt ? own[t] & 0xFFFFu : 0u;
-        uw |= v;
-        cnt[1 + t] += __popc(v);
-      }
-      cnt[0] += __popc(uw);
-    }
-#pragma unroll
-    for (int q = 0; q <= kBatchMax; ++q) {
-      const int v = wave_sum_int(cnt[q]);
-      if (lane == 0) s_cnt[wave][q] = v;
-    }
-    __syncthreads();
-    if (tid < kUgbChannels && ((u16 >> tid) & 1u)) {
-      int pre0 = 0;
-#pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) pre0 += s_cnt[w][0];
-      const uint32_t below = (1u << tid) - 1u;
-      int* ulist = reinterpret_cast<int*>(a.ws + a.off_ulist);
-      ulist[pre0 + __popc(u16 & below)] = c0 + tid;
-#pragma unroll
-      for (int t = 0; t < kBatchMax; ++t) {
-        if ((mine[t] >> tid) & 1u) {
-          int pre = 0;
-#pragma unroll
-          for (int w = 0; w < kThreads / 64; ++w) pre += s_cnt[w][1 + t];
-          a.mask_idx[static_cast<size_t>(t) * f + pre + __popc(mine[t] & below)] = c0 + tid;
-        }
-      }
-    }
-    if (blockIdx.x == gridDim.x - 1 && tid <= kBatchMax) {  // the last range: totals
-      int tot = 0;
-#pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) tot += s_cnt[w][tid];
-      if (tid == 0) {
-        reinterpret_cast<int*>(a.ws + a.off_ulist)[f] = tot + nloc;
-      } else if (tid - 1 < nt) {
-        a.mask_count[tid - 1] = tot + __popc(mine[tid - 1]);
-      }
-    }
-  }
-  if (nloc == 0) return;  // block-uniform
-
+  load_tile(0);
   f32x4_t C = {0.f, 0.f, 0.f, 0.f};
   const int m = lane & 15;  // A row = token
   const int brow = 16 * chh + n;
@@ -451,16 +459,8 @@ size_t down_batch_smem(const DownBatchArgs& a) {
 }
 
 hipError_t launch_upgate_batch(const UpGateBatchArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.f / kUgbChannels));  // f % 128 == 0
-  const int passes = (a.f / 32 + kThreads - 1) / kThreads;
-  if (passes <= 1)
-    hipLaunchKernelGGL(upgate_batch_kernel<1>, grid, dim3(kThreads), 0, s, a);
-  else if (passes <= 2)
-    hipLaunchKernelGGL(upgate_batch_kernel<2>, grid, dim3(kThreads), 0, s, a);
-  else if (passes <= 4)
-    hipLaunchKernelGGL(upgate_batch_kernel<4>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(upgate_batch_kernel<8>, grid, dim3(kThreads), 0, s, a);  // f <= 65536
+  const int blocks = (a.f + kUgbChannels - 1) / kUgbChannels;
+  hipLaunchKernelGGL(upgate_batch_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
