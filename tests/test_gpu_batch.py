@@ -88,6 +88,7 @@ def _check_tokens(ov, xs_host, out, tau_x, tau_s, label, act="silu"):
     (256, 768, "f32", 5, 65),       # fp32 weights: grouped Stage 1, per-token Stage 2
     (64, 128, "bf16", 4, 66),       # minimum shape
     (1024, 2560, "bf16", 17, 67),   # three groups: 8 + 8 + 1
+    (3072, 24576, "bf16", 4, 68),   # 768 rows per Stage-1 split: a full and a ragged 512-row pass
 ])
 def test_grouped_decode_parity(P, d, f, dtype, batch, seed):
     layer = synth.make_layer(_cfg(d, f, dtype, seed, batch), n_dec=batch)
