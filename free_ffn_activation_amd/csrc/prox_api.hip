@@ -182,8 +182,8 @@ UpGateBatchArgs upgate_batch_args(const Plan& p, const prox_layer* L, const void
   a.ws = static_cast<uint8_t*>(ws);
   a.tok_bytes = p.tok_bytes;
   a.off_bitmap = p.off_bitmap;
-  a.off_ssp = p.off_ssp;
   a.off_ulist = p.off_ulist;
+  a.off_arows = p.off_arows;
   a.mask_idx = mask_idx;
   a.mask_count = mask_count;
   return a;
@@ -200,8 +200,8 @@ DownBatchArgs down_batch_args(const Plan& p, const prox_layer* L, void* ws, int 
   a.w_down = L->w_down;
   a.ws = static_cast<uint8_t*>(ws);
   a.tok_bytes = p.tok_bytes;
-  a.off_ssp = p.off_ssp;
   a.off_ulist = p.off_ulist;
+  a.off_arows = p.off_arows;
   a.off_dpart = p.off_dpart;
   return a;
 }
@@ -517,6 +517,8 @@ Plan make_plan(int d, int f, int wdtype) {
   off = align256(off + static_cast<size_t>(f) * 4);
   p.off_ulist = off;
   off = align256(off + static_cast<size_t>(f + 64) * 4);
+  p.off_arows = off;
+  off = align256(off + static_cast<size_t>(f) * 16 * 2);
   p.off_dpart = off;
   off = align256(off + static_cast<size_t>(p.dnb_groups) * d * 4);
   p.tok_bytes = off;

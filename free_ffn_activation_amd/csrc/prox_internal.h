@@ -47,6 +47,7 @@ struct Plan {
   // workspace layout, bytes per token and offsets inside a token's slice
   size_t tok_bytes;
   size_t off_tickets, off_kcount, off_partial, off_bitmap, off_ssp;
+  size_t off_arows;  // grouped path: per union ordinal, the tokens' s as bf16 (hi, lo) pairs [f][16]
   size_t off_ulist;  // group's first token: union channel list [f] + count at [f]
   size_t off_dpart;  // batched down partials [dnb_groups][d] fp32
 };
@@ -77,7 +78,7 @@ struct UpGateBatchArgs {
   const void* w_upgate_t;  // [f][2][d] bf16
   const void* x;           // [nt][d] bf16
   uint8_t* ws;
-  size_t tok_bytes, off_bitmap, off_ssp, off_ulist;
+  size_t tok_bytes, off_bitmap, off_ulist, off_arows;
   int* mask_idx;           // [nt][f]
   int* mask_count;         // [nt]
 };
@@ -86,7 +87,7 @@ struct DownBatchArgs {
   int d, f, nt, col_slices, groups, max_rows;
   const void* w_down;      // [f][d] bf16
   uint8_t* ws;
-  size_t tok_bytes, off_ssp, off_ulist, off_dpart;
+  size_t tok_bytes, off_ulist, off_arows, off_dpart;
 };
 
 struct UpGateArgs {

@@ -24,7 +24,8 @@
 //     ordinals; 32-row tiles of W_down (1 KB per row) are staged in LDS and
 //     ds_read_b64_tr_b16 turns them into B operands (8 rows of one column per
 //     lane).  A rows are (token, part): s split into a bf16 high and low part
-//     (~16 significant bits; products exact, fp32 accumulation).  Each block
+//     (~16 significant bits; products exact, fp32 accumulation), stored per
+//     union ordinal by the up/gate kernel and loaded as rows.  Each block
 //     writes its partial y; down_reduce_kernel adds the groups in fixed order,
 //     so y is reproducible bit for bit.
 #include "prox_device.h"
@@ -279,16 +280,22 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
 #pragma unroll
   for (int i = 0; i < 4; ++i)  // lane n < 8 receives lane n + 8 (gate of the same channel)
     gt[i] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(C[i]), 0x128, 0xF, 0xF, false));
+  // s of tokens 4g..4g+3 (0 where the token does not keep the channel, and
+  // for token slots past nt), stored as the down kernel's A-row entries:
+  // ordinal o holds (hi, lo) bf16 pairs of tokens 0..7, 32 bytes
   if (n < 8 && g < 2 && slot < nloc) {
     const uint32_t tb = s_tb[slot];
+    uint32_t pk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * g + i;
-      if (t < nt) {
-        float* ssp = reinterpret_cast<float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_ssp);
-        ssp[j] = ((tb >> t) & 1u) ? C[i] * gate_act(gt[i], a.act) : 0.f;
-      }
+      const float sv = (t < nt && ((tb >> t) & 1u)) ? C[i] * gate_act(gt[i], a.act) : 0.f;
+      const uint32_t hi = f32_to_bf16_rne(sv);
+      const uint32_t lo = f32_to_bf16_rne(sv - __uint_as_float(hi << 16));
+      pk[i] = hi | (lo << 16);
     }
+    u32x4_t* ar = reinterpret_cast<u32x4_t*>(a.ws + a.off_arows) + static_cast<size_t>(u0 + slot) * 2 + g;
+    *ar = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
   }
 }
 
@@ -316,40 +323,28 @@ __global__ __launch_bounds__(kDnbThreads) void down_batch_kernel(DownBatchArgs a
   uint16_t* wb = reinterpret_cast<uint16_t*>(smem);
   uint16_t* As = wb + 2 * kDnbTileRows * kDnbCols;
   int* ul = reinterpret_cast<int*>(As + static_cast<size_t>(a.max_rows) * 16);
+  // the group's channels, and its A rows as the up/gate kernel stored them
+  // (ordinal o: m = 2t + part, s_t split into bf16 hi and lo), both in one
+  // round trip; rows past the group (the last tile's padding) are zero
   for (int r = tid; r < nr; r += kDnbThreads) ul[r] = min(max(ulist[o0 + r], 0), f - 1);
-  __syncthreads();
-  // A: rows r of the group, m = 2t + part: s_t[ul[r]] split into bf16 hi and
-  // lo.  The gathers of 8 entries per thread are issued before any is used,
-  // so the fill costs one memory round trip per 8 entries, not one per entry.
-  constexpr int kAfill = 8;
-  const int nidx = ntile * kDnbTileRows * kBatchMax;
-  for (int i0 = 0; i0 < nidx; i0 += kAfill * kDnbThreads) {  // block-uniform
-    float sv[kAfill];
+  {
+    const u32x4_t* arow = reinterpret_cast<const u32x4_t*>(a.ws + a.off_arows);
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int r = tid; r < ntile * kDnbTileRows; r += kDnbThreads) {
+      const u32x4_t v0 = r < nr ? arow[static_cast<size_t>(o0 + r) * 2] : z;
+      const u32x4_t v1 = r < nr ? arow[static_cast<size_t>(o0 + r) * 2 + 1] : z;
+      const int kt = r / kDnbTileRows;
+      const int k = r % kDnbTileRows;
+      uint16_t* at = As + static_cast<size_t>(kt) * 512 + ((k >> 3) * 16) * 8 + (k & 7);
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int u = 0; u < kAfill; ++u) {
-      const int idx = i0 + u * kDnbThreads + tid;
-      const int r = idx / kBatchMax;
-      const int t = idx % kBatchMax;
-      sv[u] = (idx < nidx && r < nr && t < nt)
-                  ? reinterpret_cast<const float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_ssp)[ul[r]]
-                  : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kAfill; ++u) {
-      const int idx = i0 + u * kDnbThreads + tid;
-      if (idx < nidx) {
-        const int r = idx / kBatchMax;
-        const int t = idx % kBatchMax;
-        const uint16_t hi = f32_to_bf16_rne(sv[u]);
-        const uint16_t lo = f32_to_bf16_rne(sv[u] - __uint_as_float(static_cast<uint32_t>(hi) << 16));
-        const int kt = r / kDnbTileRows;
-        const int k = r % kDnbTileRows;
-        uint16_t* at = As + static_cast<size_t>(kt) * 512 + ((k >> 3) * 16) * 8 + (k & 7);
-        at[(2 * t) * 8] = hi;
-        at[(2 * t + 1) * 8] = lo;
+      for (int q = 0; q < 8; ++q) {
+        at[(2 * q) * 8] = static_cast<uint16_t>(w[q] & 0xFFFFu);
+        at[(2 * q + 1) * 8] = static_cast<uint16_t>(w[q] >> 16);
       }
     }
   }
+  __syncthreads();
 
   // staging: thread -> (16-B unit u = tid % 64, rows tid / 64 + 8q); unit u of
   // row r sits at unit u ^ (2 * (r & 3)) (conflict-free transposed reads)
