@@ -427,23 +427,32 @@ __global__ __launch_bounds__(kDnbThreads) void down_batch_kernel(DownBatchArgs a
   }
 }
 
-// kG >= a.groups: every group's partial is loaded unconditionally (indices
-// past the last group re-read it and are not added), so all loads are in
-// flight before the first use; the sum keeps the fixed group order.
+// 64 outputs per block; wave q adds groups [q kG/4, (q + 1) kG/4) of them
+// (kG >= a.groups: every partial in the range is loaded unconditionally,
+// indices past the last group re-read it and are not added, so all loads are
+// in flight before the first use), then wave 0 adds the four sums as
+// (q0 + q1) + (q2 + q3): a fixed order, so y is reproducible bit for bit.
 template <int kG>
 __global__ __launch_bounds__(kThreads) void down_reduce_kernel(DownBatchArgs a, float* y) {
-  const int idx = blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= a.nt * a.d) return;
-  const int t = idx / a.d;
-  const int c = idx - t * a.d;
+  constexpr int kPer = kG / 4;
+  __shared__ float s_part[4][64];
+  const int lane = threadIdx.x & 63;
+  const int q = threadIdx.x >> 6;
+  const int idx = blockIdx.x * 64 + lane;
+  const bool on = idx < a.nt * a.d;
+  const int ii = on ? idx : 0;
+  const int t = ii / a.d;
+  const int c = ii - t * a.d;
   const float* dp = reinterpret_cast<const float*>(a.ws + static_cast<size_t>(t) * a.tok_bytes + a.off_dpart) + c;
-  float v[kG];
+  float v[kPer];
 #pragma unroll
-  for (int u = 0; u < kG; ++u) v[u] = dp[static_cast<size_t>(min(u, a.groups - 1)) * a.d];
-  float s = 0.f;
+  for (int u = 0; u < kPer; ++u) v[u] = dp[static_cast<size_t>(min(q * kPer + u, a.groups - 1)) * a.d];
+  float sum = 0.f;
 #pragma unroll
-  for (int u = 0; u < kG; ++u) s += u < a.groups ? v[u] : 0.f;
-  y[idx] = s;
+  for (int u = 0; u < kPer; ++u) sum += q * kPer + u < a.groups ? v[u] : 0.f;
+  s_part[q][lane] = sum;
+  __syncthreads();
+  if (q == 0 && on) y[idx] = (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
 }
 
 }  // namespace
@@ -465,7 +474,7 @@ hipError_t launch_down_batch(const DownBatchArgs& a, float* y, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.nt * a.d;
-  const dim3 rgrid(static_cast<unsigned>((n + kThreads - 1) / kThreads));
+  const dim3 rgrid(static_cast<unsigned>((n + 63) / 64));
   if (a.groups <= 8)
     hipLaunchKernelGGL(down_reduce_kernel<8>, rgrid, dim3(kThreads), 0, s, a, y);
   else if (a.groups <= 16)
