@@ -55,6 +55,11 @@ constexpr int kRowsPerLoad = kS1bThreads / 8;    // 32 rows per load round (8 th
 constexpr int kLoads = kChunkRows / kRowsPerLoad;  // 16 loads of 16 B per thread per pass
 constexpr int kLoadsPerPhase = kPhaseRows / kRowsPerLoad;  // 4
 
+static_assert(kChunkRows == 2 * kS1bThreads, "the mask step gives each thread two rows of a pass");
+static_assert(kLoads % 4 == 0, "a thread's gather offsets are read as 16-byte vectors");
+static_assert(2 * kPw == kS1bThreads, "the last block loads one output (up or gate column) per thread");
+static_assert(kBatchMax % kS1bWaves == 0, "the last block's waves form the tokens' states in turn");
+
 // LDS: the A operands of one pass [mat][tile][half][k-group][m][8], the staged
 // code rows of one phase, the pass's union-row offsets, per-wave statistics.
 struct S1BShared {
@@ -359,6 +364,7 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(3))
   // thread o loads output o (up, then gate, of the panel's columns) of every
   // token for 8 splits at a time (fixed split order in the sums); then wave w
   // forms the state and mask bits of tokens w and w + 4
+  static_assert(sizeof(float) * kBatchMax * 2 * kPw <= sizeof(S1BShared::B), "split sums fit the staging buffer");
   float* sv = reinterpret_cast<float*>(sh.B);  // [token][2 * kPw]
   const int o = tid;
   const int mm = o / kPw;  // 0 = up, 1 = gate
