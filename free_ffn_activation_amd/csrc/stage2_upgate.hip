@@ -155,7 +155,10 @@ __global__ __launch_bounds__(kUgThreads) void upgate_kernel(UpGateArgs a) {
   const int f = a.f;
   const int nchunks = d / kEpl;
   const int nsteps = (nchunks + 63) / 64;
-  const int gw = static_cast<int>(blockIdx.x) * kWaves + wave;
+  // ordinal gw, gw + nwaves, ...: consecutive ordinals go to consecutive
+  // blocks, so the waves left without a channel (ordinals past k_s) spread
+  // over every CU instead of filling the last blocks
+  const int gw = wave * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
   const int nwaves = static_cast<int>(gridDim.x) * kWaves;
 
   // ---- prologue: bitmap (decode mode) or list count, then x; one round trip
