@@ -89,6 +89,7 @@ def _check_tokens(ov, xs_host, out, tau_x, tau_s, label, act="silu"):
     (64, 128, "bf16", 4, 66),       # minimum shape
     (1024, 2560, "bf16", 17, 67),   # three groups: 8 + 8 + 1
     (3072, 24576, "bf16", 4, 68),   # 768 rows per Stage-1 split: a full and a ragged 512-row pass
+    (5120, 25600, "bf16", 3, 69),   # Qwen3-32B shape: 1280 rows per split, three passes (512, 512, 256)
 ])
 def test_grouped_decode_parity(P, d, f, dtype, batch, seed):
     layer = synth.make_layer(_cfg(d, f, dtype, seed, batch), n_dec=batch)
