@@ -27,7 +27,9 @@ Readings where the pages are silent (each also listed in the design notes):
   R4  threshold tests are inclusive (>=), as printed.
   R5  Stage 2 uses the dense x.
   R6  tau_s is calibrated on |proxy state| with input sparsity applied.
-  R7  calibration thresholds are exact order statistics.
+  R7  calibration thresholds are exact order statistics; the keep fractions
+      are the fp32 values the C ABI receives, so n = ceil(fp32(keep) * N)
+      (fp32(0.3) is slightly above 0.3: at N = 1280 that keeps 385, not 384).
   R10 SiLU(z) = z / (1 + exp(-z)).
   R13 empty masks give zero output.
   R14 index lists are ascending.
@@ -253,8 +255,10 @@ def calibrate(X_cal, q_up, sc_up, q_gate, sc_gate, keep_x: float, sparsity_s: fl
     [blog] "evidence" section (calibration paragraph): fixed per-layer scalar
     thresholds from activation samples.  tau_x keeps the fraction keep_x of
     the pooled |x| (C1); tau_s keeps 1 - sparsity_s of the pooled |s~|, where
-    s~ is the proxy state under tau_x (C2, reading R6).  keep fractions are
-    evaluated as double(1) - double(sparsity) so both sides count alike.
+    s~ is the proxy state under tau_x (C2, reading R6).  Both fractions are
+    the fp32 values the C ABI receives, widened exactly: n = ceil(fp32(keep_x)
+    * N) for tau_x and n = ceil((1 - fp32(sparsity_s)) * N) in double for
+    tau_s (reading R7).
     """
     return calibrate_with(X_cal, lambda xt, tx: proxy_state(xt, q_up, sc_up, q_gate, sc_gate, tx, act)["s"],
                           keep_x, sparsity_s)
@@ -272,7 +276,9 @@ def calibrate_with(X_cal, state_fn, keep_x: float, sparsity_s: float):
     state s~ of one token under the fp32 input threshold tau_x."""
     X = np.asarray(X_cal, dtype=np.float64)
     ax = np.abs(X).ravel()
-    tau_x = order_statistic_keep(ax, n_keep(float(keep_x), ax.size))
+    # keep fractions arrive as fp32 values (the ABI's type), widened exactly:
+    # ceil(keep * N) is taken on that fp32 value (reading R7)
+    tau_x = order_statistic_keep(ax, n_keep(float(np.float32(keep_x)), ax.size))
     tau_x32 = float(np.float32(tau_x)) if math.isfinite(tau_x) else math.inf
     s_all = np.concatenate([np.abs(state_fn(X[t], tau_x32)) for t in range(X.shape[0])])
     keep_s = 1.0 - float(np.float32(sparsity_s))

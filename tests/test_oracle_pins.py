@@ -257,6 +257,23 @@ def test_calibration_bruteforce():
     assert sum(1 for v in svals if v >= tau_s) == nks
 
 
+def test_calibration_keep_fraction_is_the_fp32_value():
+    """keep_x reaches the library as an fp32 value; fp32(0.3) is slightly
+    above 0.3, so with N = 1280 pooled values ceil(fp32(0.3) N) = 385 while
+    ceil(0.3 N) in double is 384.  The oracle must keep 385 (brute force)."""
+    assert math.ceil(0.3 * 1280) == 384
+    assert math.ceil(float(np.float32(0.3)) * 1280) == 385
+    cfg = synth.LayerConfig("small", 32, 48, "f32", 0.05, 2, 20.0, 40, 0.5, 0.7, 1, 29)
+    Wu, Wg, Wd, _, Xc = _f64(synth.make_layer(cfg))   # N = 40 x 32 = 1280 values
+    qu, su = oracle.pack_proxy(Wu)
+    qg, sg = oracle.pack_proxy(Wg)
+    tau_x, _ = oracle.calibrate(Xc, qu, su, qg, sg, 0.3, 0.7)
+    vals = sorted(abs(v) for v in Xc.ravel())
+    assert len(vals) == 1280
+    assert tau_x == float(np.float32(vals[1280 - 385]))
+    assert sum(1 for v in vals if v >= tau_x) == 385   # no ties in Laplace draws
+
+
 def test_n_keep_edges():
     assert oracle.n_keep(0.0, 10) == 0 and oracle.n_keep(1.0, 10) == 10
     assert oracle.n_keep(0.5, 7) == 4
