@@ -21,31 +21,7 @@ Y_MAX_ABS = 2e-2
 Y_REL_L2 = 1e-2
 
 
-def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
-
-
-def wdtype_code(dtype: str) -> int:
-    from free_ffn_activation_amd import prox
-    return prox.PROX_BF16 if dtype == "bf16" else prox.PROX_F32
-
-
-def pack_layer(layer: synth.Layer, device="cuda", activation: int = 0):
-    """Upload W_up/W_gate/W_down and run prox_pack_proxy.  Returns ProxLayer
-    (activation: 0 SiLU / SwiGLU, 1 GELU-tanh / GeGLU)."""
-    from free_ffn_activation_amd import prox
-    cfg = layer.cfg
-    L = prox.ProxLayer(cfg.d_model, cfg.d_ff, wdtype_code(cfg.dtype), device=device,
-                       activation=activation)
-    wu = to_device(layer.w_up, cfg.dtype, device)
-    wg = to_device(layer.w_gate, cfg.dtype, device)
-    wd = to_device(layer.w_down, cfg.dtype, device)
-    prox.prox_pack_proxy(wu, wg, wd, L)
-    torch.cuda.synchronize()
-    del wu, wg, wd
-    return L
+from free_ffn_activation_amd.upload import pack_layer, to_device, wdtype_code  # noqa: F401  (re-exported)
 
 
 @functools.lru_cache(maxsize=4)
@@ -100,6 +76,31 @@ def band_compare(mask_idx: np.ndarray, count: int, s_oracle: np.ndarray, tau_s: 
     band = np.abs(np.abs(s_oracle) - tau_s) <= MASK_BAND_REL * tau_s
     diff = gpu != ref
     return int(np.sum(diff & ~band)), int(np.sum(diff & band)), ascending
+
+
+def band_disagreements(mask_idx: np.ndarray, count: int, s_oracle: np.ndarray, tau_s: float) -> np.ndarray:
+    """Distances | |s~_j| - tau_s | (oracle s~) of the channels where the GPU
+    list and the oracle mask disagree."""
+    f = s_oracle.size
+    J = np.asarray(mask_idx[:count], dtype=np.int64)
+    gpu = np.zeros(f, dtype=bool)
+    gpu[J[(J >= 0) & (J < f)]] = True
+    diff = gpu != oracle.channel_mask(s_oracle, tau_s)
+    return np.abs(np.abs(s_oracle[diff]) - tau_s)
+
+
+# A GPU proxy state is within S_TILDE_TOL * max|s~| of the oracle's (the
+# proxy-state parity rule), so a channel can only be classified differently
+# when its oracle |s~| lies that close to tau_s.
+S_TILDE_TOL = 1e-5
+
+
+def check_in_band(mask_idx: np.ndarray, count: int, s_oracle: np.ndarray, tau_s: float, label: str) -> None:
+    """Bound on the in-band disagreements: each must be one the proxy-state
+    tolerance explains (oracle |s~| within S_TILDE_TOL * max|s~| of tau_s)."""
+    dist = band_disagreements(mask_idx, count, s_oracle, tau_s)
+    lim = S_TILDE_TOL * float(np.max(np.abs(s_oracle))) if s_oracle.size else 0.0
+    assert np.all(dist <= lim), f"{label}: in-band disagreement {dist.max():.3e} > {lim:.3e}"
 
 
 def y_errors(y_gpu: np.ndarray, y_ref: np.ndarray):

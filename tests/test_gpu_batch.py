@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import synth
-from prox_gpu_util import band_compare, oracle_layer, oracle_view, pack_layer, to_device, y_errors, y_ok
+from prox_gpu_util import band_compare, check_in_band, oracle_layer, oracle_view, pack_layer, to_device, y_errors, y_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,7 @@ def _check_tokens(ov, xs_host, out, tau_x, tau_s, label, act="silu"):
         oob, inb, asc = band_compare(mi[k], int(mc[k]), ref["s_tilde"], tau_s)
         assert asc, f"{label} token {k}: index list not ascending / in range"
         assert oob == 0, f"{label} token {k}: {oob} channel(s) outside the band disagree"
+        check_in_band(mi[k], int(mc[k]), ref["s_tilde"], tau_s, f"{label} token {k}")
         band += inb
         m = np.zeros(len(ref["s_tilde"]), bool)
         m[mi[k][: mc[k]]] = True

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from prox_gpu_util import (band_compare, decode_proxy_bytes, oracle_layer, oracle_view,
+from prox_gpu_util import (band_compare, check_in_band, decode_proxy_bytes, oracle_layer, oracle_view,
                            pack_layer, to_device, y_errors, y_ok)
 
 pytestmark = pytest.mark.gpu
@@ -64,6 +64,7 @@ def _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, label, act="silu"):
         oob, inb, asc = band_compare(mi[k], int(mc[k]), ref["s_tilde"], tau_s)
         assert asc, f"{label} token {t}: index list not ascending / in range"
         assert oob == 0, f"{label} token {t}: {oob} channel(s) outside the band disagree"
+        check_in_band(mi[k], int(mc[k]), ref["s_tilde"], tau_s, f"{label} token {t}")
         total_band += inb
         # y against the oracle's Stage 2 on the GPU's own channel list
         m_gpu = np.zeros(L.d_ff, bool)
@@ -163,6 +164,50 @@ def test_decode_parity(P, name, tokens):
     tau_x, tau_s = _oracle_taus(ov, n_tok=None if name == "tiny" else 16)
     for t in tokens:
         _run_decode(P, L, layer, ov, [t], tau_x, tau_s, f"{name}")
+
+
+@pytest.fixture(scope="module")
+def layer8b(P):
+    layer, ov = oracle_layer("qwen3_8b")
+    return layer, ov, pack_layer(layer)
+
+
+# Operating points the benchmark times beside the headline (keep_x 0.5,
+# s2 0.7): the 36-layer sweep's s2 = 0.5 and 0.6, the pages' own point from
+# the computation-budget section (e = 0.7 at s1 = 0.7 with alpha = 1/3 gives
+# s2 = 0.7667, keep_x = 0.3), and the allocator's point for e = 0.7 at s1 = 0.7
+# with the alpha measured on MI355X (0.759: s2 = 0.8519).  Thresholds are the
+# oracle's, calibrated on 16 tokens; keep_x 0.3 is not exact in fp32.
+@pytest.mark.parametrize("keep_x,s2", [(0.5, 0.5), (0.5, 0.6), (0.3, 0.7667), (0.3, 0.8519)])
+def test_decode_operating_points_8b(P, layer8b, keep_x, s2):
+    layer, ov, L = layer8b
+    if s2 == 0.8519:
+        assert abs(oracle.stage2_sparsity_for_target(0.7, 0.7, 0.759) - s2) < 5e-5
+        assert abs(P.prox_budget_s2(0.7, 0.7, 0.759) - s2) < 5e-5
+    if s2 == 0.7667:
+        assert abs(oracle.stage2_sparsity_for_target(0.7, 0.7, 1.0 / 3.0) - s2) < 5e-5
+    tau_x, tau_s = _oracle_taus(ov, keep_x=keep_x, sparsity_s=s2, n_tok=16)
+    _y, _mi, mc, ic = _run_decode(P, L, layer, ov, [0, 1], tau_x, tau_s, f"8b keep_x={keep_x} s2={s2}")
+    # the runtime keep fractions land near the calibrated ones (16 tokens)
+    assert abs(float(np.mean(ic)) / L.d_model - keep_x) < 0.05
+    assert abs(float(np.mean(mc)) / L.d_ff - (1.0 - s2)) < 0.05
+
+
+def test_calibrate_keep_fraction_fp32(P):
+    """keep_x = 0.3 with N a multiple of 10 (320 x 16 = 5120 fp32 values): the
+    library counts ceil(fp32(0.3) N) = 1537, as does the oracle; tau_x is
+    bit-exact, tau_s within 1e-5."""
+    layer = synth.make_layer(_small_cfg(320, 384, "f32", 47), n_dec=1)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    xc = to_device(layer.x_cal, "f32")              # fp32 Laplace draws: no ties
+    assert xc.shape[0] * 320 == 5120
+    ws = torch.empty(P.prox_calibrate_workspace_size(320, 384, xc.shape[0]), dtype=torch.uint8, device="cuda")
+    tx, ts = P.prox_calibrate(L, xc, 0.3, 0.7667, ws)
+    rx, rs = _oracle_taus(ov, 0.3, 0.7667)
+    assert np.float32(tx) == np.float32(rx)
+    assert abs(ts - rs) <= 1e-5 * rs
+    assert int(np.sum(np.abs(ov["x_cal"]) >= rx)) == 1537
 
 
 def test_decode_batch8_per_token_masks(P):

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from prox_gpu_util import band_compare, oracle_layer, oracle_view, to_device, y_errors, y_ok
+from prox_gpu_util import band_compare, check_in_band, oracle_layer, oracle_view, to_device, y_errors, y_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +78,7 @@ def _decode_check(P, L16, layer, ov, tokens, tau_x, tau_s, label):
         assert ic[k] == ref["k_x"], f"{label} token {t}: k_x"
         oob, inb, asc = band_compare(mi[k], int(mc[k]), ref["s_tilde"], tau_s)
         assert asc and oob == 0, f"{label} token {t}: {oob} channel(s) outside the band disagree"
+        check_in_band(mi[k], int(mc[k]), ref["s_tilde"], tau_s, f"{label} token {t}")
         band += inb
         m = np.zeros(L16.d_ff, bool)
         m[mi[k][: mc[k]]] = True
