@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libprox.so")
+# PROX_LIBRARY selects another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("PROX_LIBRARY") or os.path.join(_HERE, "libprox.so")
 
 PROX_OK = 0
 PROX_ERR_INVALID_ARG = -1

@@ -1,0 +1,187 @@
+"""The Stage-1 split-K hand-off, checked on the CPU (no GPU needed).
+
+Every Stage-1 kernel splits its input rows over several blocks per output
+panel; each block writes its partial sums to the workspace and takes a ticket,
+and the block that draws the last ticket adds the partials in fixed split
+order.  The hand-off uses no cache-wide maintenance.  Its correctness rests on
+two things this file checks:
+
+1. The gfx950 code the compiler generates keeps the sequence: partials
+   stored with agent-coherent stores (sc1, written through to the level all
+   XCDs share), every storing thread waiting for its stores (s_waitcnt
+   vmcnt(0)) and the block synchronising (s_barrier) before the ticket
+   atomic; after the atomic, a wait and a block barrier before any
+   agent-coherent (sc1) load of the partials; and no buffer_wbl2 or
+   buffer_inv anywhere in the kernel.  A compiler or flag change that moved
+   a load above the ticket, dropped a coherence bit or the wait fails here.
+2. A model of the protocol (blocks as interleaved event sequences, stores
+   becoming visible at arbitrary later times unless waited for): over many
+   random schedules the last-ticket block always reads every fresh partial,
+   exactly one block reduces, the ticket returns to 0 for the next call, and
+   the result is bit-identical whatever the arrival order.  Without the wait
+   the model finds schedules that read a stale partial (negative control).
+"""
+import os
+import random
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "free_ffn_activation_amd", "csrc")
+
+# (source, kernel-name substring) of every kernel with the split-K hand-off
+HANDOFF_KERNELS = [("stage1.hip", "stage1_kernel"), ("stage1_batch.hip", "stage1_batch_kernel"),
+                   ("stage1_w16.hip", "stage1_w16_kernel")]
+
+
+def _hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    return None
+
+
+def _device_asm(src: str, tmp_path) -> str:
+    from free_ffn_activation_amd import build_lib
+    flags = [f for f in build_lib.FLAGS if f not in ("-shared", "-fPIC")]
+    out = os.path.join(str(tmp_path), src + ".s")
+    cmd = [_hipcc(), *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
+           os.path.join(CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    with open(out) as fh:
+        return fh.read()
+
+
+def _kernel_bodies(asm: str, name_part: str):
+    """{symbol: [instruction lines]} for the kernels whose symbol contains name_part."""
+    bodies, cur, name = {}, None, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            name = m.group(1)
+            cur = [] if name_part in name else None
+            if cur is not None:
+                bodies[name] = cur
+            continue
+        if cur is None:
+            continue
+        ins = line.split(";")[0].strip()
+        if not ins or ins.startswith(".") or ins.endswith(":"):
+            continue
+        cur.append(ins)
+        if ins.startswith("s_endpgm"):
+            cur = None
+    return bodies
+
+
+def _is_sc1_store(i):
+    return i.startswith("global_store") and re.search(r"\bsc1\b", i) is not None
+
+
+def _is_sc1_load(i):
+    return i.startswith("global_load") and re.search(r"\bsc1\b", i) is not None
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+@pytest.mark.parametrize("src,kernel", HANDOFF_KERNELS)
+def test_handoff_sequence_in_generated_code(src, kernel, tmp_path):
+    bodies = _kernel_bodies(_device_asm(src, tmp_path), kernel)
+    assert bodies, f"no {kernel} in the generated code of {src}"
+    for sym, ins in bodies.items():
+        assert not any(i.startswith(("buffer_wbl2", "buffer_inv")) for i in ins), \
+            f"{sym}: cache-wide maintenance in the kernel"
+        tickets = [k for k, i in enumerate(ins) if i.startswith("global_atomic_add")]
+        assert len(tickets) == 1, f"{sym}: expected one ticket atomic, found {len(tickets)}"
+        t = tickets[0]
+        assert "sc0" in ins[t].split(), f"{sym}: the ticket atomic must return its value"
+        stores = [k for k in range(t) if _is_sc1_store(ins[k])]
+        assert stores, f"{sym}: no agent-coherent partial store before the ticket"
+        # after the last agent-coherent store: a full vmcnt wait, then a barrier, then the ticket
+        between = ins[stores[-1] + 1:t]
+        w = [k for k, i in enumerate(between) if re.match(r"s_waitcnt\s+vmcnt\(0\)", i)]
+        b = [k for k, i in enumerate(between) if i.startswith("s_barrier")]
+        assert w and b and w[0] < b[-1], f"{sym}: stores not waited for and synchronised before the ticket"
+        # no plain store of partial data may follow the coherent ones before the ticket
+        assert not any(i.startswith("global_store") for i in between), f"{sym}: store between wait and ticket"
+        # no agent-coherent load before the ticket; after it a wait and a barrier precede the first one
+        assert not any(_is_sc1_load(i) for i in ins[:t]), f"{sym}: partial load above the ticket"
+        loads = [k for k in range(t + 1, len(ins)) if _is_sc1_load(ins[k])]
+        assert loads, f"{sym}: no agent-coherent partial load after the ticket"
+        after = ins[t + 1:loads[0]]
+        w2 = [k for k, i in enumerate(after) if re.match(r"s_waitcnt\s+vmcnt\(0\)", i)]
+        b2 = [k for k, i in enumerate(after) if i.startswith("s_barrier")]
+        assert w2 and b2 and w2[0] < b2[0], f"{sym}: partials read before the ticket's result was shared"
+
+
+# ---------------------------------------------------------------- protocol model
+def _simulate(splits, partials, rng, with_wait=True, ticket0=0):
+    """One call of the hand-off for one panel under a random schedule.
+
+    Block b: store its partial (issued), [wait until visible], take a ticket;
+    the block drawing splits-1 reads all partials (a partial not yet visible
+    reads as the stale value NaN) and adds them in split order, then resets
+    the ticket.  A store becomes visible at any later step of the schedule.
+    Returns (sum, reducers, final ticket, stale reads)."""
+    memory = [np.float32(np.nan)] * splits        # stale contents from an earlier call
+    pending = {}                                   # block -> value issued, not yet visible
+    state = {b: "store" for b in range(splits)}
+    ticket = ticket0
+    reducers, total, stale = [], None, 0
+    while True:
+        moves = []
+        for b, st in state.items():
+            if st == "store":
+                moves.append(("store", b))
+            elif st == "ticket" and (not with_wait or b not in pending):
+                moves.append(("ticket", b))
+        moves += [("visible", b) for b in pending]
+        if not moves:
+            break
+        kind, b = rng.choice(moves)
+        if kind == "store":
+            pending[b] = partials[b]
+            state[b] = "ticket"
+        elif kind == "visible":
+            memory[b] = pending.pop(b)
+        else:
+            prev = ticket
+            ticket += 1
+            state[b] = "done"
+            if prev == splits - 1:
+                reducers.append(b)
+                acc = np.float32(0.0)
+                for k in range(splits):               # fixed split order
+                    v = memory[k]
+                    stale += int(np.isnan(v))
+                    acc = np.float32(acc + v)
+                total = acc
+                ticket = 0                            # ready for the next call
+    for b, v in pending.items():
+        memory[b] = v
+    return total, reducers, ticket, stale
+
+
+def test_ticket_protocol_model():
+    rng = random.Random(7)
+    for splits in (2, 3, 8, 16):
+        partials = [np.float32(v) for v in np.random.default_rng(splits).standard_normal(splits)]
+        ref = np.float32(0.0)
+        for v in partials:
+            ref = np.float32(ref + v)
+        for _ in range(400):
+            total, reducers, ticket, stale = _simulate(splits, partials, rng)
+            assert len(reducers) == 1 and ticket == 0 and stale == 0
+            assert np.float32(total).view(np.uint32) == ref.view(np.uint32)   # bit-identical
+
+
+def test_ticket_protocol_model_needs_the_wait():
+    """Negative control: without waiting for its stores before the ticket, a
+    block can hand over before its partial is visible."""
+    rng = random.Random(11)
+    partials = [np.float32(v) for v in range(1, 9)]
+    stale = sum(_simulate(8, partials, rng, with_wait=False)[3] for _ in range(400))
+    assert stale > 0
