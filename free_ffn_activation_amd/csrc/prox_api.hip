@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -216,10 +217,10 @@ hipError_t for_each_group(int32_t batch, Fn fn) {
   return hipSuccess;
 }
 
-prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, float tau_x,
-                        float tau_s, float* y, int32_t* mask_idx, int32_t* mask_count,
-                        int32_t* in_count, void* ws, size_t ws_bytes, void* stream,
-                        void* const* events, int32_t stages = 7) {
+// Checks of prox_ffn_decode's arguments other than the workspace.
+prox_status check_decode_args(const prox_layer* layer, const void* x, int32_t batch, float tau_x, float tau_s,
+                              const float* y, const int32_t* mask_idx, const int32_t* mask_count,
+                              const int32_t* in_count) {
   prox_status st = check_layer(layer);
   if (st != PROX_OK) return st;
   if ((st = check_batch(batch)) != PROX_OK) return st;
@@ -230,6 +231,15 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mask_idx, 4) || !aligned(mask_count, 4) ||
       (in_count && !aligned(in_count, 4)))
     return fail(PROX_ERR_INVALID_ARG, "x and y must be 16-byte aligned, index buffers 4-byte aligned");
+  return PROX_OK;
+}
+
+prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, float tau_x,
+                        float tau_s, float* y, int32_t* mask_idx, int32_t* mask_count,
+                        int32_t* in_count, void* ws, size_t ws_bytes, void* stream,
+                        void* const* events, int32_t stages = 7) {
+  prox_status st = check_decode_args(layer, x, batch, tau_x, tau_s, y, mask_idx, mask_count, in_count);
+  if (st != PROX_OK) return st;
   const Plan p = make_plan(layer->d_model, layer->d_ff, layer->wdtype);
   if ((st = check_ws(p, batch, ws, ws_bytes)) != PROX_OK) return st;
   if (events) {
@@ -917,6 +927,77 @@ PROX_API prox_status prox_proxy_state(const prox_layer* layer, const void* x, in
     }
     if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
     return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode.  The workspace is the file-scope device array
+// `scratch` (one copy per GPU, held until the process ends).  In host code the
+// array's name is only a handle for hipGetSymbolAddress: the device address
+// of each GPU's copy is looked up once per device, with that device current,
+// and only that address is passed to kernels and fills.
+namespace {
+
+constexpr size_t kScratchBytes = static_cast<size_t>(32) << 20;  // PROX_NOALLOC_SCRATCH_BYTES
+static_assert(kScratchBytes == PROX_NOALLOC_SCRATCH_BYTES, "scratch size and header disagree");
+
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Per device: the address of its scratch copy and the layout (shape, tokens)
+// whose must-be-zero words (the Stage-1 tickets) are known to be zero.
+struct ScratchState {
+  uint8_t* ptr = nullptr;
+  int d = 0, f = 0, batch = 0;
+};
+std::mutex g_scratch_mu;
+std::vector<ScratchState> g_scratch;
+
+}  // namespace
+
+PROX_API prox_status prox_ffn_decode_noalloc(const prox_layer* layer, const void* x, int32_t batch, float tau_x,
+                                             float tau_s, float* y, int32_t* mask_idx, int32_t* mask_count,
+                                             int32_t* in_count, void* stream) {
+  try {
+    g_err.clear();
+    prox_status st = check_decode_args(layer, x, batch, tau_x, tau_s, y, mask_idx, mask_count, in_count);
+    if (st != PROX_OK) return st;
+    const Plan p = make_plan(layer->d_model, layer->d_ff, layer->wdtype);
+    const size_t need = p.tok_bytes * static_cast<size_t>(batch);
+    if (need > kScratchBytes)
+      return fail(PROX_ERR_UNSUPPORTED,
+                  "d_model=%d d_ff=%d batch=%d needs %zu bytes of scratch, above the %zu bytes the allocation-free "
+                  "entry point holds per GPU (use prox_ffn_decode with a workspace)",
+                  layer->d_model, layer->d_ff, batch, need, kScratchBytes);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0) return fail(PROX_ERR_INTERNAL, "hipGetDevice returned %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch.size() <= static_cast<size_t>(dev)) g_scratch.resize(static_cast<size_t>(dev) + 1);
+    ScratchState& sc = g_scratch[static_cast<size_t>(dev)];
+    if (sc.ptr == nullptr) {  // once per device, with that device current
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (addr == nullptr) return fail(PROX_ERR_INTERNAL, "hipGetSymbolAddress(scratch) gave NULL");
+      sc.ptr = static_cast<uint8_t*>(addr);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Every completed call leaves its tickets at zero; another shape moves the
+    // token slices (and their tickets) onto bytes that held other data, and a
+    // larger batch reaches slices not used before: clear the region then.
+    // (A fill kernel, not a memset, so a captured call replays correctly.)
+    if (sc.d != layer->d_model || sc.f != layer->d_ff || batch > sc.batch) {
+      e = launch_fill_zero(sc.ptr, need, s);
+      if (e != hipSuccess) return hip_fail(e, "scratch fill");
+      sc.d = layer->d_model;
+      sc.f = layer->d_ff;
+      sc.batch = batch;
+    }
+    return decode_impl(layer, x, batch, tau_x, tau_s, y, mask_idx, mask_count, in_count, sc.ptr, kScratchBytes,
+                       stream, nullptr);
   } catch (...) {
     return fail(PROX_ERR_INTERNAL, "unexpected exception");
   }

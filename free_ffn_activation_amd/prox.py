@@ -40,7 +40,7 @@ _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPO
 EXPORTED = ("prox_abi_version", "prox_last_error", "prox_layer_sizes", "prox_workspace_size",
             "prox_calibrate_workspace_size", "prox_budget_effective", "prox_budget_s2",
             "prox_workspace_init", "prox_pack_proxy", "prox_proxy16_size", "prox_pack_proxy16",
-            "prox_calibrate", "prox_calibrate_hist_workspace_size", "prox_calibrate_hist", "prox_ffn_decode", "prox_ffn_decode_events",
+            "prox_calibrate", "prox_calibrate_hist_workspace_size", "prox_calibrate_hist", "prox_ffn_decode", "prox_ffn_decode_noalloc", "prox_ffn_decode_events",
             "prox_ffn_decode_stages", "prox_ffn_stage2", "prox_proxy_state")
 
 
@@ -84,6 +84,8 @@ _sig = {
                                 _P(_c_f32), _c_vp, _c_size, _c_vp]),
     "prox_ffn_decode": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_vp, _c_vp,
                                  _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+    "prox_ffn_decode_noalloc": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_vp, _c_vp,
+                                         _c_vp, _c_vp, _c_vp]),
     "prox_ffn_decode_events": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_vp,
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp, _P(_c_vp)]),
     "prox_ffn_decode_stages": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_vp,
@@ -326,6 +328,18 @@ def prox_ffn_decode(layer: ProxLayer, x: torch.Tensor, tau_x: float, tau_s: floa
     _check(_lib.prox_ffn_decode(ctypes.byref(layer.desc), _ptr(x), b, tau_x, tau_s, _ptr(y),
                                 _ptr(mask_idx), _ptr(mask_count), _ptr(in_count), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)))
+
+
+PROX_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def prox_ffn_decode_noalloc(layer: ProxLayer, x: torch.Tensor, tau_x: float, tau_s: float,
+                            y: torch.Tensor, mask_idx: torch.Tensor, mask_count: torch.Tensor,
+                            in_count: torch.Tensor | None, stream=None) -> None:
+    """prox_ffn_decode on the library's per-GPU scratch array (no workspace)."""
+    b = _decode_args(layer, x, y, mask_idx, mask_count, in_count)
+    _check(_lib.prox_ffn_decode_noalloc(ctypes.byref(layer.desc), _ptr(x), b, tau_x, tau_s, _ptr(y),
+                                        _ptr(mask_idx), _ptr(mask_count), _ptr(in_count), _stream(stream)))
 
 
 def prox_ffn_decode_events(layer: ProxLayer, x: torch.Tensor, tau_x: float, tau_s: float,

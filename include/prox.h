@@ -266,6 +266,32 @@ prox_status prox_ffn_decode(const prox_layer* layer, const void* x, int32_t batc
                             size_t ws_bytes, void* stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  Same arguments, results and kernels as
+ * prox_ffn_decode, without `ws` / `ws_bytes`: the workspace is a file-scope
+ * device array of PROX_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * copy per GPU, held until the process ends.  The call allocates and frees
+ * nothing (no hipMalloc, no allocating library routine).
+ *   - prox_workspace_size(d_model, d_ff, batch) must not exceed
+ *     PROX_NOALLOC_SCRATCH_BYTES, else PROX_ERR_UNSUPPORTED and nothing is
+ *     enqueued (32 MiB holds, e.g., 18 tokens of the Qwen3-8B-shaped layer
+ *     and 14 of the Qwen3-32B-shaped one).
+ *   - The first call on a GPU, and a call whose shape differs from the
+ *     previous call's on that GPU or whose batch exceeds every earlier one,
+ *     also enqueues a fill kernel that clears the used part of the array.
+ *   - Every call on one GPU uses that GPU's array: calls that overlap in time
+ *     on one GPU (other streams, other host threads) race and give wrong
+ *     results; serialise them, e.g. on one stream.  The array keeps the last
+ *     call's contents.
+ * Asynchronous (kernels on `stream`).
+ */
+#define PROX_NOALLOC_SCRATCH_BYTES (32u << 20)
+prox_status prox_ffn_decode_noalloc(const prox_layer* layer, const void* x, int32_t batch,
+                                    float tau_x, float tau_s, float* y, int32_t* mask_idx,
+                                    int32_t* mask_count, int32_t* in_count, void* stream);
+
+/*
  * prox_ffn_decode that also records four hipEvent_t (host array `events`,
  * passed as void*): [0] before Stage 1, [1] after Stage 1, [2] after the
  * Stage-2 up/gate kernel, [3] after the down kernel.  For timing only.

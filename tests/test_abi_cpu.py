@@ -165,3 +165,19 @@ def test_proxy16_sizes_and_pack_validation():
     assert lib.prox_pack_proxy16(FAKE, FAKE, ctypes.byref(_layer(proxy_w16=FAKE)), None) == P.PROX_ERR_UNSUPPORTED
     assert lib.prox_pack_proxy16(FAKE + 8, FAKE, ctypes.byref(_layer(dt=P.PROX_BF16, proxy_w16=FAKE)), None) == \
         P.PROX_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_before_touching_a_device():
+    """The allocation-free entry point validates like prox_ffn_decode and
+    refuses a size beyond its scratch array before any device call."""
+    lib = P.raw_library()
+    L = _layer(4096, 12288, P.PROX_BF16)
+    per_token = P.prox_workspace_size(4096, 12288, 1)
+    too_many = P.PROX_NOALLOC_SCRATCH_BYTES // per_token + 1
+    st = lib.prox_ffn_decode_noalloc(ctypes.byref(L), FAKE, too_many, 0.5, 0.1, FAKE, FAKE, FAKE, None, None)
+    assert st == P.PROX_ERR_UNSUPPORTED and "scratch" in P.prox_last_error()
+    st = lib.prox_ffn_decode_noalloc(ctypes.byref(L), FAKE, 1, math.nan, 0.1, FAKE, FAKE, FAKE, None, None)
+    assert st == P.PROX_ERR_INVALID_ARG
+    st = lib.prox_ffn_decode_noalloc(None, FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE, None, None)
+    assert st == P.PROX_ERR_INVALID_ARG
+    assert P.PROX_NOALLOC_SCRATCH_BYTES == 32 << 20
