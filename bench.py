@@ -75,13 +75,14 @@ def log(msg: str) -> None:
 # two kernels, whose counters add up).
 KERNELS = {
     "stage1_proxy": (("stage1.hip",), ("stage1_kernel<prox::Bf16Tag, false>",)),
-    "stage2_upgate": (("stage2_upgate.hip",), ("upgate_kernel<prox::Bf16Tag, true>",)),
-    "stage2_down": (("stage2_down.hip",), ("down_kernel<prox::Bf16Tag, true>",)),
+    "stage2_fused": (("stage2_fused.hip", "stage2_common.h"), ("stage2_fused_kernel<prox::Bf16Tag>",)),
+    "stage2_upgate": (("stage2_upgate.hip", "stage2_common.h"), ("upgate_kernel<prox::Bf16Tag, true>",)),
+    "stage2_down": (("stage2_down.hip", "stage2_common.h"), ("down_kernel<prox::Bf16Tag, true>",)),
     "stage1_proxy_batch": (("stage1_batch.hip",), ("stage1_batch_kernel<prox::Bf16Tag, false>",)),
     "stage2_upgate_batch": (("stage2_batch.hip",), ("upgate_batch_kernel",)),
     "stage2_down_batch": (("stage2_batch.hip",), ("down_batch_kernel", "down_reduce_kernel")),
 }
-STAGE_NAMES = ["stage1_proxy", "stage2_upgate", "stage2_down"]
+STAGE_NAMES = ["stage1_proxy", "stage2_upgate", "stage2_down"]  # the decode step's kernels
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -300,10 +301,11 @@ def decode_counts(rot, taus, layers=None, out=None):
 
 def byte_model(kx, ks, d: int, f: int, w: int):
     """Algorithmic bytes per (layer, token): the whole step and each kernel."""
+    ug = 2 * ks * d * w + d * w + f // 8 + 8 * ks
+    dn = ks * d * w + 8 * ks + 4 * d
     return {"step": kx * f + 8 * kx + 3 * ks * d * w + d * w + 4 * d + 4 * ks,
             "stage1_proxy": kx * f + 8 * kx + d * w + f // 8,
-            "stage2_upgate": 2 * ks * d * w + d * w + f // 8 + 8 * ks,
-            "stage2_down": ks * d * w + 8 * ks + 4 * d}
+            "stage2_upgate": ug, "stage2_down": dn, "stage2_fused": ug + dn}
 
 
 def per_step_events(rot, fn, n: int):
@@ -385,23 +387,31 @@ def measure_decode(rot, taus, K: int, workload: str, keep_x: float, sparsity_s: 
         for s in range(spr):
             full(s)
         torch.cuda.synchronize()
-        bits = [prox.PROX_STAGE_PROXY, prox.PROX_STAGE_UPGATE, prox.PROX_STAGE_DOWN]
-        k_us = [time_graph(staged(b), spr, K, f"{workload} {nm} alone", graph=not args.no_graph)
-                for nm, b in zip(STAGE_NAMES, bits)]
+        # the step's three kernels, then the fused Stage-2 kernel (opt-in,
+        # PROX_STAGE_FUSED_STAGE2) for comparison
+        fused = prox.PROX_STAGE_FUSED_STAGE2
+        runs = [("stage1_proxy", prox.PROX_STAGE_PROXY), ("stage2_upgate", prox.PROX_STAGE_UPGATE),
+                ("stage2_down", prox.PROX_STAGE_DOWN),
+                ("stage2_fused", prox.PROX_STAGE_UPGATE | prox.PROX_STAGE_DOWN | fused)]
+        k_us = {nm: time_graph(staged(b), spr, K, f"{workload} {nm} alone", graph=not args.no_graph)
+                for nm, b in runs}
+        if not args.no_graph:
+            res["us_per_layer_fused_stage2"] = round(
+                time_graph(staged(7 | fused), spr, K, f"{workload} decode, Stage 2 fused (opt-in)"), 3)
         del iso
-        kb = [rot.tmean(bm[nm], K) for nm in STAGE_NAMES]
-        dom = int(np.argmax(k_us))
+        kb = {nm: rot.tmean(bm[nm], K) for nm, _ in runs}
+        dom = max(STAGE_NAMES, key=lambda nm: k_us[nm])
         ach = kb[dom] / (k_us[dom] * 1e-6) / 1e9
         key = traffic_key(workload, d, f, keep_x, sparsity_s, 1)
-        traffic = measured_traffic(STAGE_NAMES[dom], key, kb[dom])
-        res["kernels"] = {STAGE_NAMES[i]: {"us": round(k_us[i], 3), "algorithmic_MB": round(kb[i] / 1e6, 3),
-                                           "GBps": round(kb[i] / (k_us[i] * 1e-6) / 1e9, 1)} for i in range(3)}
-        res["roofline"] = {"bound": "hbm", "kernel": STAGE_NAMES[dom], "achieved": round(ach, 1),
+        traffic = measured_traffic(dom, key, kb[dom])
+        res["kernels"] = {nm: {"us": round(k_us[nm], 3), "algorithmic_MB": round(kb[nm] / 1e6, 3),
+                               "GBps": round(kb[nm] / (k_us[nm] * 1e-6) / 1e9, 1)} for nm, _ in runs}
+        res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                            "traffic": traffic["bytes_per_launch"] if traffic else None,
                            "traffic_detail": traffic, "algorithmic_bytes_per_launch": round(kb[dom]),
                            "traffic_key": key}
-        log(f"{workload} kernels alone: " + ", ".join(f"{nm} {u:.2f}" for nm, u in zip(STAGE_NAMES, k_us)))
+        log(f"{workload} kernels alone: " + ", ".join(f"{nm} {u:.2f}" for nm, u in k_us.items()))
     if dense and not args.no_dense and rot.cfg.dtype == "bf16":
         res["dense_us_per_layer"] = dense_comparators(rot, K, o, args)
     return res, kx, ks

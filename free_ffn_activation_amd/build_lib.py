@@ -24,7 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libprox.so")
 LIB_HOSTSAN = os.path.join(PKG, "libprox_hostsan.so")
 SOURCES = ["prox_api.hip", "stage1.hip", "stage1_batch.hip", "stage2_upgate.hip", "stage2_down.hip",
-           "stage2_batch.hip", "stage1_w16.hip", "pack.hip"]
+           "stage2_fused.hip", "stage2_batch.hip", "stage1_w16.hip", "pack.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/prox.h: argument validation,
 // launch planning, workspace layout and calibration orchestration.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -217,6 +218,61 @@ hipError_t for_each_group(int32_t batch, Fn fn) {
   return hipSuccess;
 }
 
+FusedArgs fused_args(const Plan& p, const prox_layer* L, const void* x, void* ws, int* mask_idx, int* mask_count,
+                     float* y, uint32_t wait_ticks) {
+  FusedArgs a;
+  a.ug = upgate_args(p, L, x, ws, mask_idx, mask_count, y);
+  a.w_down = L->w_down;
+  a.col_slices = p.fz_col_slices;
+  a.row_groups = p.fz_row_groups;
+  a.chan_per_group = p.fz_chan_per_group;
+  a.max_rows = p.fz_max_rows;
+  a.red_bytes = p.fz_red_bytes;
+  a.off_flags = p.off_flags;
+  a.off_err = p.off_err;
+  a.wait_ticks = wait_ticks;
+  return a;
+}
+
+std::atomic<uint32_t> g_wait_ticks{kDefaultWaitTicks};
+
+// Per device: the CU count and the fused Stage-2 kernel's resident blocks per
+// CU for each (weight dtype, LDS bytes) seen.
+struct DevInfo {
+  int cus = 0;
+  std::vector<std::pair<std::pair<int, size_t>, int>> occ;
+};
+std::mutex g_dev_mu;
+std::vector<DevInfo> g_dev;
+
+// Grid of the fused Stage-2 kernel on the current device (one block per CU),
+// or 0 when it cannot run there: fewer than one resident block per CU, more
+// CUs than the workspace holds barrier flags for, or a failed query (the two
+// Stage-2 kernels run instead).
+int fused_grid(int wdtype, size_t smem) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (g_dev.size() <= static_cast<size_t>(dev)) g_dev.resize(static_cast<size_t>(dev) + 1);
+  DevInfo& di = g_dev[static_cast<size_t>(dev)];
+  if (di.cus == 0 && hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    di.cus = 0;
+    return 0;
+  }
+  int occ = -1;
+  for (const auto& e : di.occ)
+    if (e.first.first == wdtype && e.first.second == smem) occ = e.second;
+  if (occ < 0) {
+    if (fused_occupancy(wdtype, smem, &occ) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    di.occ.push_back({{wdtype, smem}, occ});
+  }
+  if (occ < 1 || di.cus < 1 || di.cus > kMaxGridFlags) return 0;
+  return di.cus;
+}
+
 // Checks of prox_ffn_decode's arguments other than the workspace.
 prox_status check_decode_args(const prox_layer* layer, const void* x, int32_t batch, float tau_x, float tau_s,
                               const float* y, const int32_t* mask_idx, const int32_t* mask_count,
@@ -246,10 +302,10 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
     for (int i = 0; i < 4; ++i)
       if (!events[i]) return fail(PROX_ERR_INVALID_ARG, "events[%d] is NULL", i);
   }
-  if ((stages & 7) == 0 || stages < 0 || stages > 31 ||
+  if ((stages & 7) == 0 || stages < 0 || stages > 63 ||
       ((stages & PROX_STAGE_PER_TOKEN) && (stages & PROX_STAGE_GROUPED)))
-    return fail(PROX_ERR_INVALID_ARG, "stages %d: a non-empty subset of 1|2|4, plus at most one of 8 and 16",
-                stages);
+    return fail(PROX_ERR_INVALID_ARG, "stages %d: a non-empty subset of 1|2|4, plus at most one of 8 and 16, "
+                "and optionally 32", stages);
   // Kernels per group of nt <= kBatchMax tokens: the grouped ones (each proxy
   // row and channel of the group's unions read once; Stage 2 grouped for bf16
   // weights, INT4 proxy only) from kGroupedMinTokens tokens up, where they are
@@ -292,7 +348,19 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
   }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  if (stages & PROX_STAGE_UPGATE) {
+  // batch 1, both Stage-2 kernels and PROX_STAGE_FUSED_STAGE2: one fused
+  // launch where the device can hold its grid
+  int fgrid = 0;
+  FusedArgs fa;
+  if (batch == 1 && (stages & PROX_STAGE_UPGATE) && (stages & PROX_STAGE_DOWN) &&
+      (stages & PROX_STAGE_FUSED_STAGE2)) {
+    fa = fused_args(p, layer, x, ws, mask_idx, mask_count, y, g_wait_ticks.load());
+    fgrid = fused_grid(layer->wdtype, fused_smem(fa));
+  }
+  if (fgrid > 0) {
+    e = launch_stage2_fused(fa, layer->wdtype, fgrid, s);
+    if (e != hipSuccess) return hip_fail(e, "fused stage-2 launch");
+  } else if (stages & PROX_STAGE_UPGATE) {
     if (!any2) {
       e = launch_upgate(upgate_args(p, layer, x, ws, mask_idx, mask_count, y), layer->wdtype, batch,
                         p.ug_blocks, true, s);
@@ -309,7 +377,7 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
   }
   if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[2]), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  if (stages & PROX_STAGE_DOWN) {
+  if ((stages & PROX_STAGE_DOWN) && fgrid == 0) {
     if (!any2) {
       e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, true, s);
     } else {
@@ -513,8 +581,26 @@ Plan make_plan(int d, int f, int wdtype) {
   gb = std::max(1, std::min({gb, f / 32, 64}));  // at most 64 groups: the reduction holds one value per group
   p.dnb_groups = gb;
   p.dnb_max_rows = ((f + gb - 1) / gb + 31) / 32 * 32;
+  // fused Stage 2 (batch 1): the same column slices, about kFusedItems items
+  // (one per block of the grid), a row group at most one channel per thread;
+  // LDS: max(x, the 16 waves' partial rows) + (index, s) per row
+  p.fz_col_slices = p.dn_col_slices;
+  {
+    int frg = std::max(1, kFusedItems / p.fz_col_slices);
+    frg = std::max(frg, (f + kFusedThreads - 1) / kFusedThreads);
+    p.fz_chan_per_group = ((f + frg - 1) / frg + 31) / 32 * 32;
+    p.fz_row_groups = (f + p.fz_chan_per_group - 1) / p.fz_chan_per_group;
+    p.fz_max_rows = p.fz_chan_per_group;
+    const int fz_red = (kFusedThreads / 64) * cw * 4;
+    const int x_bytes = d * static_cast<int>(elem_size(wdtype));
+    p.fz_red_bytes = (std::max(fz_red, x_bytes) + 15) / 16 * 16;
+  }
   // per-token workspace slice
   size_t off = 0;
+  p.off_err = off;  // error word of the bounded waits
+  off = align256(off + 4);
+  p.off_flags = off;  // grid-barrier flags of the fused Stage-2 kernel
+  off = align256(off + static_cast<size_t>(kMaxGridFlags) * 4);
   p.off_tickets = off;
   off = align256(off + static_cast<size_t>(p.n_panels) * 4);
   p.off_kcount = off;
@@ -1001,4 +1087,33 @@ PROX_API prox_status prox_ffn_decode_noalloc(const prox_layer* layer, const void
   } catch (...) {
     return fail(PROX_ERR_INTERNAL, "unexpected exception");
   }
+}
+
+PROX_API prox_status prox_workspace_check(const void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    if (!ws || !aligned(ws, 256)) return fail(PROX_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+    if (ws_bytes < 4) return fail(PROX_ERR_INVALID_ARG, "workspace of %zu bytes holds no error word", ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "error word copy");
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "workspace check synchronisation");
+    if (word == 0u) return PROX_OK;
+    e = launch_fill_zero(const_cast<void*>(ws), sizeof(word), s);
+    if (e != hipSuccess) return hip_fail(e, "error word clear");
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "workspace check synchronisation");
+    return fail(PROX_ERR_INTERNAL,
+                "a decode on this workspace gave up waiting at the fused Stage-2 grid barrier (error word 0x%x): "
+                "its blocks were not all resident within the wait limit; its y was not computed", word);
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_set_wait_limit(uint32_t ticks, uint32_t* previous) {
+  g_err.clear();
+  const uint32_t old = g_wait_ticks.exchange(ticks);
+  if (previous) *previous = old;
+  return PROX_OK;
 }

@@ -18,6 +18,10 @@ constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads
 constexpr int kUgThreads = 256;        // up/gate kernel: threads per block
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
 constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column slice
+constexpr int kFusedThreads = 1024;    // fused Stage-2 kernel: 16 waves per block, one block per CU
+constexpr int kFusedItems = 256;       // fused Stage-2 kernel: down items planned (the CU count of MI355X)
+constexpr int kMaxGridFlags = 1024;    // fused Stage-2 kernel: grid-barrier flags in the workspace
+constexpr uint32_t kDefaultWaitTicks = 4000000u;  // bounded waits: 40 ms of the 100 MHz real-time clock
 constexpr int kBatchMax = 8;           // tokens per group of the batched kernels
 constexpr int kGroupedMinTokens = 3;   // smaller groups run the per-token kernels (faster there)
 
@@ -44,8 +48,13 @@ struct Plan {
   int dnb_col_slices;
   int dnb_groups;
   int dnb_max_rows;  // rows per group, multiple of 32
-  // workspace layout, bytes per token and offsets inside a token's slice
+  // fused Stage 2 (batch 1): down items of (column slice, row group)
+  int fz_col_slices, fz_row_groups, fz_chan_per_group, fz_max_rows, fz_red_bytes;
+  // workspace layout, bytes per token and offsets inside a token's slice; the
+  // error word and the grid-barrier flags sit at fixed offsets at the start
+  // of a slice (shape-independent)
   size_t tok_bytes;
+  size_t off_err, off_flags;
   size_t off_tickets, off_kcount, off_partial, off_bitmap, off_ssp;
   size_t off_arows;  // grouped path: per union ordinal, the tokens' s as bf16 (hi, lo) pairs [f][16]
   size_t off_ulist;  // group's first token: union channel list [f] + count at [f]
@@ -113,12 +122,25 @@ struct DownArgs {
   float* y;
 };
 
+// Fused Stage 2 of one token (batch 1): up/gate then down in one launch.
+struct FusedArgs {
+  UpGateArgs ug;          // decode mode; ug.ws_mut is token 0's workspace slice
+  const void* w_down;     // [f][d]
+  int col_slices, row_groups, chan_per_group, max_rows;
+  int red_bytes;          // LDS bytes before the row list: max(x, down reduction buffer)
+  size_t off_flags, off_err;
+  uint32_t wait_ticks;    // bounded wait of the grid barrier (100 MHz clock ticks)
+};
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_state,
                          hipStream_t s);
 hipError_t launch_upgate(const UpGateArgs& a, int wdtype, int batch, int blocks,
                          bool from_bitmap, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, int wdtype, int batch, bool from_bitmap, hipStream_t s);
+hipError_t launch_stage2_fused(const FusedArgs& a, int wdtype, int grid, hipStream_t s);
+hipError_t fused_occupancy(int wdtype, size_t smem, int* blocks_per_cu);
+size_t fused_smem(const FusedArgs& a);
 hipError_t launch_stage1_batch(const Stage1Args& a, int wdtype, bool write_state, hipStream_t s);
 hipError_t launch_stage1_w16(const Stage1Args& a, int batch, bool write_state, hipStream_t s);
 int proxy16_row_stride(int f);

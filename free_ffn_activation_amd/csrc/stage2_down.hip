@@ -19,34 +19,10 @@
 //     slice into y with fp32 atomics (y was zeroed by the up/gate kernel).
 //     Large blocks keep the atomic count (row groups x d) low: fp32 global
 //     atomics cost far more per byte than the weight stream.
-#include "prox_device.h"
-#include "prox_internal.h"
+#include "stage2_common.h"
 
 namespace prox {
 namespace {
-
-template <typename T>
-__device__ __forceinline__ void axpy16(float* acc, float s, uint4 w);
-
-template <>
-__device__ __forceinline__ void axpy16<Bf16Tag>(float* acc, float s, uint4 w) {
-  acc[0] = fmaf(s, bf16lo(w.x), acc[0]);
-  acc[1] = fmaf(s, bf16hi(w.x), acc[1]);
-  acc[2] = fmaf(s, bf16lo(w.y), acc[2]);
-  acc[3] = fmaf(s, bf16hi(w.y), acc[3]);
-  acc[4] = fmaf(s, bf16lo(w.z), acc[4]);
-  acc[5] = fmaf(s, bf16hi(w.z), acc[5]);
-  acc[6] = fmaf(s, bf16lo(w.w), acc[6]);
-  acc[7] = fmaf(s, bf16hi(w.w), acc[7]);
-}
-
-template <>
-__device__ __forceinline__ void axpy16<F32Tag>(float* acc, float s, uint4 w) {
-  acc[0] = fmaf(s, __uint_as_float(w.x), acc[0]);
-  acc[1] = fmaf(s, __uint_as_float(w.y), acc[1]);
-  acc[2] = fmaf(s, __uint_as_float(w.z), acc[2]);
-  acc[3] = fmaf(s, __uint_as_float(w.w), acc[3]);
-}
 
 template <typename T, bool kFromBitmap>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
@@ -73,28 +49,15 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
   int n = 0;
   if (kFromBitmap) {
     // decode mode: this block's rows are the kept channels of a fixed channel
-    // range; the bitmap word and s_j of each channel come in one round trip
-    // and a block ballot compacts them in ascending order
+    // range, compacted from the bitmap; s_j (stored by channel index) of each
+    // thread's channel is read in the same round trip
     const int c0 = rg * a.chan_per_group;
     const int c1 = min(f, c0 + a.chan_per_group);
-    const int j = c0 + tid;
-    const int jc = min(j, c1 - 1);
-    const uint32_t word = reinterpret_cast<const uint32_t*>(tws + a.off_bitmap)[jc >> 5];
-    const float sj = ssp[jc];
-    const bool kept = j < c1 && ((word >> (jc & 31)) & 1u);
-    const uint64_t bal = __ballot(kept);
-    if (lane == 0) s_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = 0;
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      if (w2 < wave) off += s_cnt[w2];
-      n += s_cnt[w2];
-    }
-    if (kept) {
-      const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
-      jr[pos] = j;
-      sr[pos] = sj;
-    }
+    const float sj = ssp[min(c0 + tid, c1 - 1)];
+    int slot;
+    n = s2::compact_range<kDownThreads>(s2::range_word(reinterpret_cast<const uint32_t*>(tws + a.off_bitmap), c0, c1),
+                                        c0, c1, jr, s_cnt, slot);
+    if (slot >= 0) sr[slot] = sj;
   } else {
     const int ks = min(max(a.mask_count[b], 0), f);
     const int per = (ks + a.row_groups - 1) / a.row_groups;
@@ -113,40 +76,20 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
 
   const int col = cs * kCw + lane * kEpl;
   const bool cvalid = col < d;
-  const S* Wd = static_cast<const S*>(a.w_down);
+  const uint8_t* Wd = static_cast<const uint8_t*>(a.w_down);
   float acc[kEpl];
 #pragma unroll
   for (int e = 0; e < kEpl; ++e) acc[e] = 0.f;
-  // Loads are unconditional: a slot past the end (or a skipped index) re-reads
-  // a valid row with weight 0, and a lane past the last column reads the
-  // slice's first column, so the compiler can wait on the loads one by one.
   const int colc = cvalid ? col : cs * kCw;
+  const uint32_t row_bytes = static_cast<uint32_t>(d * sizeof(S));
+  const uint32_t col_bytes = static_cast<uint32_t>(colc * sizeof(S));
   for (int i0 = wave; i0 < n; i0 += kWaves * kDownUnroll) {
     uint4 w[kDownUnroll];
-    float sv[kDownUnroll];
-#pragma unroll
-    for (int u = 0; u < kDownUnroll; ++u) {
-      const int i = min(i0 + u * kWaves, n - 1);
-      const int j = jr[i];
-      sv[u] = (i0 + u * kWaves < n && j >= 0 && cvalid) ? sr[i] : 0.f;
-      w[u] = ldg16(Wd + static_cast<size_t>(j >= 0 ? j : 0) * d + colc);
-    }
+    s2::down_batch_loads<kWaves>(Wd, row_bytes, col_bytes, jr, n, i0, w);
     __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
-#pragma unroll
-    for (int u = 0; u < kDownUnroll; ++u) axpy16<T>(acc, sv[u], w[u]);
+    s2::down_batch_fma<T, kWaves>(acc, jr, sr, n, i0, cvalid, w);
   }
-#pragma unroll
-  for (int e = 0; e < kEpl; ++e) red[wave * kCw + lane * kEpl + e] = acc[e];
-  __syncthreads();
-  for (int c = tid; c < kCw; c += kDownThreads) {
-    const int gc = cs * kCw + c;
-    if (gc < d) {
-      float v = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kWaves; ++w2) v += red[w2 * kCw + c];
-      unsafeAtomicAdd(&a.y[static_cast<size_t>(b) * d + gc], v);
-    }
-  }
+  s2::down_reduce_add<kDownThreads, kCw>(red, acc, kEpl, cs, d, a.y + static_cast<size_t>(b) * d);
 }
 
 }  // namespace

@@ -33,6 +33,8 @@ PROX_STAGE_UPGATE = 2
 PROX_STAGE_DOWN = 4
 PROX_STAGE_PER_TOKEN = 8  # batch >= 2: per-token kernels for every group
 PROX_STAGE_GROUPED = 16   # batch >= 2: grouped kernels for every group (default: groups of >= 3 tokens)
+PROX_STAGE_FUSED_STAGE2 = 32  # batch 1: up/gate and down in one launch joined by a grid barrier (opt-in)
+PROX_DEFAULT_WAIT_TICKS = 4000000  # bounded in-kernel waits: 40 ms of the 100 MHz clock
 
 _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPORTED",
                  -3: "PROX_ERR_HIP", -4: "PROX_ERR_INTERNAL"}
@@ -41,7 +43,8 @@ EXPORTED = ("prox_abi_version", "prox_last_error", "prox_layer_sizes", "prox_wor
             "prox_calibrate_workspace_size", "prox_budget_effective", "prox_budget_s2",
             "prox_workspace_init", "prox_pack_proxy", "prox_proxy16_size", "prox_pack_proxy16",
             "prox_calibrate", "prox_calibrate_hist_workspace_size", "prox_calibrate_hist", "prox_ffn_decode", "prox_ffn_decode_noalloc", "prox_ffn_decode_events",
-            "prox_ffn_decode_stages", "prox_ffn_stage2", "prox_proxy_state")
+            "prox_ffn_decode_stages", "prox_ffn_stage2", "prox_proxy_state", "prox_workspace_check",
+            "prox_set_wait_limit")
 
 
 class ProxError(RuntimeError):
@@ -94,6 +97,8 @@ _sig = {
                                  _c_size, _c_vp]),
     "prox_proxy_state": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp,
                                   _c_size, _c_vp]),
+    "prox_workspace_check": (_c_i32, [_c_vp, _c_size, _c_vp]),
+    "prox_set_wait_limit": (_c_i32, [ctypes.c_uint32, _P(ctypes.c_uint32)]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -386,3 +391,16 @@ def prox_proxy_state(layer: ProxLayer, x: torch.Tensor, tau_x: float, s_tilde: t
     _check(_lib.prox_proxy_state(ctypes.byref(layer.desc), _ptr(x), b, tau_x, _ptr(s_tilde),
                                  _ptr(in_count), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)))
+
+
+def prox_workspace_check(ws: torch.Tensor, stream=None) -> None:
+    """Raises ProxError(PROX_ERR_INTERNAL) when a decode on ws gave up a
+    bounded wait (and clears the error word).  Blocking."""
+    _check(_lib.prox_workspace_check(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def prox_set_wait_limit(ticks: int) -> int:
+    """Bound of the in-kernel waits (100 MHz clock ticks); returns the old one."""
+    prev = ctypes.c_uint32(0)
+    _check(_lib.prox_set_wait_limit(int(ticks), ctypes.byref(prev)))
+    return int(prev.value)

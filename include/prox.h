@@ -248,7 +248,9 @@ prox_status prox_calibrate_hist(const prox_layer* layer, const void* X_cal, int3
  *   in_count    device [batch] int32 (k_x per token) or NULL
  *   ws          device, >= prox_workspace_size(batch) bytes, zeroed once
  * Asynchronous: kernels on `stream`, no host synchronisation.  batch 1 runs
- * three kernels.  batch >= 2 runs groups of up to 8 tokens; a group of 3 or
+ * three kernels (Stage 1, the Stage-2 up/gate gather, the down projection;
+ * prox_ffn_decode_stages can fuse the last two, see PROX_STAGE_FUSED_STAGE2).
+ * batch >= 2 runs groups of up to 8 tokens; a group of 3 or
  * more tokens runs the grouped kernels, a smaller one the per-token kernels
  * (prox_ffn_decode_stages can force either).  Grouped (the pages study
  * batch 1 and leave larger batches open, [blog] limitations section): Stage 1
@@ -323,10 +325,39 @@ prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32
  * of fewer than 3 tokens runs the per-token kernels, which are faster there);
  * not together with PROX_STAGE_PER_TOKEN */
 #define PROX_STAGE_GROUPED 16
+/* with batch 1 and both Stage-2 bits: run Stage 2 as one launch, the up/gate
+ * gather and the down projection joined by an in-kernel grid barrier (one
+ * block per CU; each block issues its first W_down rows, known from the
+ * Stage-1 mask, before it waits).  Same results up to the fp32 order of the
+ * atomic additions into y.  Measured slower than the two launches on MI355X
+ * (device-coherent stores and polls are slow while the weight stream holds the
+ * memory system); kept for comparison.  Where the device cannot hold the grid
+ * the two kernels run instead.  The barrier's wait is bounded
+ * (prox_set_wait_limit): a call whose blocks were not all resident in time
+ * (another kernel holding the GPU) sets mask_count[0] = -1 and the workspace
+ * error word (prox_workspace_check) and leaves y undefined. */
+#define PROX_STAGE_FUSED_STAGE2 32
 prox_status prox_ffn_decode_stages(const prox_layer* layer, const void* x, int32_t batch,
                                    float tau_x, float tau_s, float* y, int32_t* mask_idx,
                                    int32_t* mask_count, int32_t* in_count, void* ws,
                                    size_t ws_bytes, void* stream, int32_t stages);
+
+/*
+ * Error word of a decode workspace: PROX_ERR_INTERNAL (and the word cleared)
+ * when a call on it gave up a bounded wait (the fused Stage-2 grid barrier,
+ * see PROX_STAGE_FUSED_STAGE2), else PROX_OK.  ws device, ws_bytes >= 4.  BLOCKS
+ * (synchronises `stream`).
+ */
+prox_status prox_workspace_check(const void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Bound of the library's in-kernel waits, in ticks of the GPU's 100 MHz
+ * real-time clock, for calls enqueued after this one (process-wide; default
+ * 4,000,000 = 40 ms).  0 gives up at the first unsatisfied check; tests use it
+ * to exercise the give-up path without any wait.  *previous (host, nullable)
+ * receives the old bound.
+ */
+prox_status prox_set_wait_limit(uint32_t ticks, uint32_t* previous);
 
 /*
  * Stage 2 alone ([blog] "Stage 2") from a caller-given channel list.

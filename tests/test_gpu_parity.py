@@ -47,13 +47,16 @@ def _oracle_taus(ov, keep_x=0.5, sparsity_s=0.7, n_tok=None, act="silu"):
     return oracle.calibrate(xc, ov["qu"], ov["su"], ov["qg"], ov["sg"], keep_x, sparsity_s, act=act)
 
 
-def _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, label, act="silu"):
+def _run_decode(P, L, layer, ov, tokens, tau_x, tau_s, label, act="silu", stages=None):
     dt = layer.cfg.dtype
     x = to_device(layer.x_dec[tokens], dt)
     b = len(tokens)
     y, mi, mc, ic = _bufs(P, L, b)
     ws = P.new_workspace(L.d_model, L.d_ff, b)
-    P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, ws)
+    if stages is None:
+        P.prox_ffn_decode(L, x, tau_x, tau_s, y, mi, mc, ic, ws)
+    else:
+        P.prox_ffn_decode_stages(L, x, tau_x, tau_s, y, mi, mc, ic, ws, stages)
     torch.cuda.synchronize()
     y, mi, mc, ic = y.cpu().numpy(), mi.cpu().numpy(), mc.cpu().numpy(), ic.cpu().numpy()
     total_band = 0
@@ -605,3 +608,107 @@ def test_depth_ordered_calibration_on_a_chain(P):
                                     rx, rs)["y"] for t in range(n)])
         H = H + Y
         X = (H / np.sqrt(np.mean(H * H, axis=-1, keepdims=True) + 1e-6)).astype(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ fused Stage 2 (batch 1)
+def test_fused_and_split_stage2_agree(P, layer8b):
+    """Batch 1 runs the up/gate and down kernels as two launches;
+    PROX_STAGE_FUSED_STAGE2 runs them as one.  Same masks and counts, y equal
+    up to the order of the fp32 atomic additions."""
+    layer, ov, L = layer8b
+    tau_x, tau_s = _oracle_taus(ov, n_tok=16)
+    ws = P.new_workspace(L.d_model, L.d_ff, 1)
+    for t in range(4):
+        x = to_device(layer.x_dec[[t]], "bf16")
+        a, b = _bufs(P, L, 1), _bufs(P, L, 1)
+        P.prox_ffn_decode(L, x, tau_x, tau_s, *a, ws)
+        P.prox_ffn_decode_stages(L, x, tau_x, tau_s, *b, ws, 7 | P.PROX_STAGE_FUSED_STAGE2)
+        torch.cuda.synchronize()
+        (ya, mia, mca, ica), (yb, mib, mcb, icb) = ([v.cpu().numpy() for v in o] for o in (a, b))
+        n = int(mca[0])
+        assert n == int(mcb[0]) and int(ica[0]) == int(icb[0]) and np.array_equal(mia[0, :n], mib[0, :n])
+        assert y_errors(ya[0], yb[0].astype(np.float64))[1] <= 1e-6
+    P.prox_workspace_check(ws)  # no bounded wait gave up
+
+
+@pytest.mark.parametrize("d,f,dt,seed", [(256, 768, "f32", 101), (320, 384, "bf16", 41), (12288, 256, "bf16", 46),
+                                         (128, 33024, "bf16", 45)])
+def test_fused_stage2_parity_shapes(P, d, f, dt, seed):
+    """The fused Stage-2 kernel against the oracle on fp32, a partial column
+    slice, the largest d_model and a three-chunk bitmap, plus the degenerate
+    thresholds (all-pass, empty mask)."""
+    layer = synth.make_layer(_small_cfg(d, f, dt, seed), n_dec=3)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov)
+    fused = 7 | P.PROX_STAGE_FUSED_STAGE2
+    _run_decode(P, L, layer, ov, [0], tau_x, tau_s, f"{d}x{f} fused", stages=fused)
+    _y, mi, mc, _ic = _run_decode(P, L, layer, ov, [1], 0.0, 0.0, f"{d}x{f} fused all-pass", stages=fused)
+    assert mc[0] == f
+    y, _mi, mc, _ic = _run_decode(P, L, layer, ov, [2], 0.0, math.inf, f"{d}x{f} fused empty", stages=fused)
+    assert mc[0] == 0 and np.all(y == 0)
+
+
+def test_fused_stage2_items_beyond_the_grid(P):
+    """d_model 12288 x d_ff 11264 (bf16): 24 column slices x 11 row groups =
+    264 down items for a 256-block grid, so some blocks of the fused Stage-2
+    kernel take a second item after the grid barrier; parity against the
+    oracle, and the same masks and counts as the two-launch path."""
+    layer = synth.make_layer(_small_cfg(12288, 11264, "bf16", 48, std=0.02), n_dec=2, n_cal=4)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov)
+    _run_decode(P, L, layer, ov, [0, 1], tau_x, tau_s, "12288x11264 fused",
+                stages=7 | P.PROX_STAGE_FUSED_STAGE2)
+    _run_decode(P, L, layer, ov, [1], tau_x, tau_s, "12288x11264")
+
+
+def test_fused_stage2_wait_limit_give_up(P, layer8b):
+    """The grid barrier's wait is bounded.  With the bound forced to 0 from the
+    host, a block that finds the barrier incomplete at its first check gives
+    up at once: the call reports mask_count = -1 and the workspace error word
+    (PROX_ERR_INTERNAL from prox_workspace_check), and the kernel ends
+    normally.  Calls with the default bound on the same workspace are correct
+    again afterwards (the barrier's epochs stay consistent)."""
+    layer, ov, L = layer8b
+    tau_x, tau_s = _oracle_taus(ov, n_tok=16)
+    x = to_device(layer.x_dec[[2]], "bf16")
+    ws = P.new_workspace(L.d_model, L.d_ff, 1)
+    ref = _bufs(P, L, 1)
+    P.prox_ffn_decode_stages(L, x, tau_x, tau_s, *ref, ws, 7 | P.PROX_STAGE_FUSED_STAGE2)
+    torch.cuda.synchronize()
+    P.prox_workspace_check(ws)
+    ry, rmi, rmc, ric = (v.cpu().numpy() for v in ref)
+    fused = 7 | P.PROX_STAGE_FUSED_STAGE2
+    gave_up = 0
+    prev = P.prox_set_wait_limit(0)
+    try:
+        for _ in range(3):
+            o = _bufs(P, L, 1)
+            P.prox_ffn_decode_stages(L, x, tau_x, tau_s, *o, ws, fused)
+            torch.cuda.synchronize()
+            try:
+                P.prox_workspace_check(ws)
+                ok = True
+            except P.ProxError as e:
+                assert e.status == P.PROX_ERR_INTERNAL
+                ok = False
+            mc = int(o[2].item())
+            if ok:   # every block found the barrier complete: a normal result
+                assert mc == int(rmc[0])
+            else:
+                assert mc == -1
+                gave_up += 1
+    finally:
+        assert P.prox_set_wait_limit(prev) == 0
+    assert gave_up >= 1, "no block gave up with a zero wait bound"
+    P.prox_workspace_check(ws)  # the error word was cleared
+    for _ in range(2):
+        o = _bufs(P, L, 1)
+        P.prox_ffn_decode_stages(L, x, tau_x, tau_s, *o, ws, fused)
+        torch.cuda.synchronize()
+        P.prox_workspace_check(ws)
+        y, mi, mc, ic = (v.cpu().numpy() for v in o)
+        n = int(rmc[0])
+        assert int(mc[0]) == n and np.array_equal(mi[0, :n], rmi[0, :n])
+        assert y_errors(y[0], ry[0].astype(np.float64))[1] <= 1e-6

@@ -20,6 +20,12 @@ two things this file checks:
    exactly one block reduces, the ticket returns to 0 for the next call, and
    the result is bit-identical whatever the arrival order.  Without the wait
    the model finds schedules that read a stale partial (negative control).
+
+The opt-in fused Stage-2 kernel joins its two phases with a grid barrier of
+per-block epoch flags and bounded waits; a model of that protocol checks the
+same properties (no block passes before every block's stores are visible,
+flags consistent across launches, including launches whose blocks give up),
+with the same kind of negative control.
 """
 import os
 import random
@@ -184,4 +190,77 @@ def test_ticket_protocol_model_needs_the_wait():
     rng = random.Random(11)
     partials = [np.float32(v) for v in range(1, 9)]
     stale = sum(_simulate(8, partials, rng, with_wait=False)[3] for _ in range(400))
+    assert stale > 0
+
+
+# ---------------------------------------------------------------- fused Stage-2 grid barrier
+def _barrier_call(flags, rng, wait_limit, allow_early_flag=False):
+    """One launch of the fused Stage-2 kernel's barrier over G blocks, under a
+    random schedule.  Block b: read its own flag (epoch = flag + 1); phase A
+    (publishes its s values); store flags[b] = epoch — only after its phase-A
+    stores are complete unless allow_early_flag (the mistake the model must
+    catch); then poll every flag until all have reached the epoch, or give up
+    after wait_limit of its own polling steps.  Returns (blocks that passed
+    with some s value not yet visible, blocks that gave up)."""
+    G = len(flags)
+    epoch = {}
+    published = {b: False for b in range(G)}  # phase-A stores visible to every block
+    state = {b: "read" for b in range(G)}
+    polls = {b: 0 for b in range(G)}
+    stale, gave_up = 0, 0
+    while any(st != "done" for st in state.values()):
+        b = rng.choice([k for k, st in state.items() if st != "done"])
+        st = state[b]
+        if st == "read":
+            epoch[b] = flags[b] + 1
+            state[b] = "phaseA"
+        elif st == "phaseA":
+            state[b] = "flag" if allow_early_flag else "ack"
+            if not allow_early_flag:
+                published[b] = True      # waited for (vmcnt) before the flag
+        elif st == "ack":
+            state[b] = "flag"
+        elif st == "flag":
+            flags[b] = epoch[b]
+            state[b] = "poll"
+            if allow_early_flag and rng.random() < 0.5:
+                published[b] = True      # may become visible later
+        elif st == "poll":
+            if all(flags[k] - epoch[b] >= 0 for k in range(G)):
+                stale += int(not all(published.values()))
+                state[b] = "done"
+            else:
+                polls[b] += 1
+                if polls[b] > wait_limit:
+                    gave_up += 1
+                    state[b] = "done"
+        for k in range(G):               # late visibility of early flags' data
+            if state[k] in ("poll", "done") and not published[k] and rng.random() < 0.3:
+                published[k] = True
+    return stale, gave_up
+
+
+def test_grid_barrier_protocol_model():
+    """Epoch flags: no block passes before every block's phase-A stores are
+    visible; the flags stay equal between launches (fresh workspace: all 0);
+    a launch whose blocks give up (wait bound 0) leaves them equal too, so the
+    next launch with the normal bound is correct."""
+    rng = random.Random(3)
+    for G in (2, 5, 16):
+        flags = [0] * G
+        for call in range(60):
+            limit = 0 if call % 7 == 3 else 10 ** 9
+            stale, gave_up = _barrier_call(flags, rng, limit)
+            assert stale == 0
+            assert len(set(flags)) == 1 and flags[0] == call + 1
+            if limit > 0:
+                assert gave_up == 0
+
+
+def test_grid_barrier_protocol_model_needs_the_wait():
+    """Negative control: a flag stored before the block's own stores are
+    complete lets some block pass while an s value is not yet visible."""
+    rng = random.Random(5)
+    flags = [0] * 8
+    stale = sum(_barrier_call(flags, rng, 10 ** 9, allow_early_flag=True)[0] for _ in range(200))
     assert stale > 0
