@@ -230,6 +230,7 @@ FusedArgs fused_args(const Plan& p, const prox_layer* L, const void* x, void* ws
   a.red_bytes = p.fz_red_bytes;
   a.off_flags = p.off_flags;
   a.off_err = p.off_err;
+  a.off_done = p.off_done;
   a.wait_ticks = wait_ticks;
   return a;
 }
@@ -597,8 +598,9 @@ Plan make_plan(int d, int f, int wdtype) {
   }
   // per-token workspace slice
   size_t off = 0;
-  p.off_err = off;  // error word of the bounded waits
-  off = align256(off + 4);
+  p.off_err = off;       // error word of the bounded waits
+  p.off_done = off + 4;  // completion ticket of the fused Stage-2 kernel
+  off = align256(off + 8);
   p.off_flags = off;  // grid-barrier flags of the fused Stage-2 kernel
   off = align256(off + static_cast<size_t>(kMaxGridFlags) * 4);
   p.off_tickets = off;

@@ -51,10 +51,10 @@ struct Plan {
   // fused Stage 2 (batch 1): down items of (column slice, row group)
   int fz_col_slices, fz_row_groups, fz_chan_per_group, fz_max_rows, fz_red_bytes;
   // workspace layout, bytes per token and offsets inside a token's slice; the
-  // error word and the grid-barrier flags sit at fixed offsets at the start
-  // of a slice (shape-independent)
+  // error word, the fused kernel's completion ticket and the grid-barrier
+  // flags sit at fixed offsets at the start of a slice (shape-independent)
   size_t tok_bytes;
-  size_t off_err, off_flags;
+  size_t off_err, off_done, off_flags;
   size_t off_tickets, off_kcount, off_partial, off_bitmap, off_ssp;
   size_t off_arows;  // grouped path: per union ordinal, the tokens' s as bf16 (hi, lo) pairs [f][16]
   size_t off_ulist;  // group's first token: union channel list [f] + count at [f]
@@ -128,7 +128,7 @@ struct FusedArgs {
   const void* w_down;     // [f][d]
   int col_slices, row_groups, chan_per_group, max_rows;
   int red_bytes;          // LDS bytes before the row list: max(x, down reduction buffer)
-  size_t off_flags, off_err;
+  size_t off_flags, off_err, off_done;
   uint32_t wait_ticks;    // bounded wait of the grid barrier (100 MHz clock ticks)
 };
 

@@ -124,15 +124,16 @@ struct WaveBitmap {
 // (W = all waves), consecutive ordinals on consecutive blocks so the waves
 // left without a channel spread over every CU.  Decode mode (kFromBitmap):
 // every wave holds the Stage-1 bitmap in registers and picks its channel by
-// ordinal; block 0 publishes k_s; every wave writes its ordinal's entry of the
-// ascending index list; s_j is stored by channel index.  List mode: the
+// ordinal; block 0 publishes k_s (unless kPublishCount is false: the caller
+// then publishes it; the function returns k_s); every wave writes its
+// ordinal's entry of the ascending index list; s_j is stored by channel index.  List mode: the
 // channel comes from the caller's list and s_j is stored by list position.
 // The block also zeroes its share of y (the down projection accumulates into
 // it).  s_j and the zeros of y are written with agent-coherent stores, so a
 // later phase of the same launch on another XCD can read them once the writer
 // has waited for its stores (see the fused kernel).  smem holds x (d elements).
-template <typename T, bool kFromBitmap, int kThreadsPB>
-__device__ __forceinline__ void upgate_block(const UpGateArgs& a, int block, int nblocks, int b, uint8_t* smem) {
+template <typename T, bool kFromBitmap, int kThreadsPB, bool kPublishCount = true>
+__device__ __forceinline__ int upgate_block(const UpGateArgs& a, int block, int nblocks, int b, uint8_t* smem) {
   typedef typename T::storage S;
   constexpr int kEpl = 16 / sizeof(S);  // elements per 16-byte load
   constexpr int kWaves = kThreadsPB / 64;
@@ -165,7 +166,7 @@ __device__ __forceinline__ void upgate_block(const UpGateArgs& a, int block, int
     __hip_atomic_store(&a.y[static_cast<size_t>(b) * d + c], 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   const int ks = kFromBitmap ? bmv.total() : min(max(ks_list, 0), f);
-  if (kFromBitmap && block == 0 && tid == 0) a.mask_count[b] = ks;
+  if (kFromBitmap && kPublishCount && block == 0 && tid == 0) a.mask_count[b] = ks;
   // channel of ordinal k (-1: past the end, or an out-of-range list entry)
   auto channel_of = [&](int k, auto held) -> int {
     if (k >= ks) return -1;
@@ -258,6 +259,7 @@ __device__ __forceinline__ void upgate_block(const UpGateArgs& a, int block, int
     }
     store(k, j, su, sg);
   }
+  return ks;
 }
 
 template <typename T>

@@ -35,9 +35,10 @@
 //     workspace) and adds one.  s_j is read after the barrier with
 //     agent-coherent loads.
 //   * a block whose wait exceeds the wait limit (ticks of the 100 MHz real-
-//     time clock) gives up: it sets the workspace error word and mask_count =
-//     -1 and skips its down work, so the kernel always ends; the host reports
-//     the error word (prox_workspace_check).
+//     time clock) gives up: it sets the workspace error word and skips its
+//     down work, so the kernel always ends; the host reports the error word
+//     (prox_workspace_check).  k_s is published once per launch, by the last
+//     block to finish (a completion ticket): -1 if any block gave up.
 #include "stage2_common.h"
 
 namespace prox {
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kFusedThreads) void stage2_fused_kernel(FusedArgs a
     s_ok = 1;
   }
   // ---- phase A: up/gate over every wave of the grid (x staged at smem)
-  s2::upgate_block<T, true, kFusedThreads>(a.ug, blk, G, 0, smem);
+  const int ks = s2::upgate_block<T, true, kFusedThreads, false>(a.ug, blk, G, 0, smem);
   __syncthreads();  // x is dead: the region becomes the down reduction buffer
 
   // ---- phase B set-up: the first item's rows and its first W_down batch
@@ -111,61 +112,75 @@ __global__ __launch_bounds__(kFusedThreads) void stage2_fused_kernel(FusedArgs a
 
   // ---- grid barrier
   if (tid == 0) __hip_atomic_store(&flags[blk], s_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!has_item) return;  // nothing to wait for
-  if (wave == 0) {
-    const unsigned epoch = s_epoch;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (true) {
-      bool mine = true;
-      for (int i = lane; i < G; i += 64)
-        mine = mine && static_cast<int>(__hip_atomic_load(&flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                                        epoch) >= 0;
-      if (__ballot(!mine) == 0ull) break;
-      if (__builtin_amdgcn_s_memrealtime() - t0 > static_cast<uint64_t>(a.wait_ticks)) {
-        if (lane == 0) {
-          s_ok = 0;
-          __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(tws + a.off_err), 1u, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(a.ug.mask_count, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (has_item) {  // block-uniform; a block without down work has nothing to wait for
+    if (wave == 0) {
+      const unsigned epoch = s_epoch;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        bool mine = true;
+        for (int i = lane; i < G; i += 64)
+          mine = mine && static_cast<int>(__hip_atomic_load(&flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                                          epoch) >= 0;
+        if (__ballot(!mine) == 0ull) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > static_cast<uint64_t>(a.wait_ticks)) {
+          if (lane == 0) {
+            s_ok = 0;
+            __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(tws + a.off_err), 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+          }
+          break;
         }
-        break;
+        __builtin_amdgcn_s_sleep(1);
       }
-      __builtin_amdgcn_s_sleep(1);
+    }
+    __syncthreads();
+
+    // ---- phase B: the items of this block (skipped if it gave up: y is then invalid)
+    float* y = a.ug.y;
+    for (int item = blk, first = 1; s_ok && item < n_items; item += G, first = 0) {
+      if (!first) {
+        cs = item % a.col_slices;
+        c0 = (item / a.col_slices) * a.chan_per_group;
+        const int c1 = min(f, c0 + a.chan_per_group);
+        n = s2::compact_range<kFusedThreads>(s2::range_word(bitmap, c0, c1), c0, c1, jr, s_cnt, slot);
+      }
+      // s_j of the rows, written by other blocks in phase A
+      if (slot >= 0) sr[slot] = __hip_atomic_load(&ssp[c0 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (n > 0) {  // block-uniform
+        const int col = cs * kCw + lane * kEpl;
+        const bool cvalid = col < d;
+        const int colc = cvalid ? col : cs * kCw;
+        float acc[kEpl];
+#pragma unroll
+        for (int e = 0; e < kEpl; ++e) acc[e] = 0.f;
+        const uint32_t col_bytes = static_cast<uint32_t>(colc * sizeof(S));
+        for (int i0 = wave; i0 < n; i0 += kWaves * kDownUnroll) {
+          if (!first || i0 != wave) {  // the first batch of the first item is already in w
+            s2::down_batch_loads<kWaves>(Wd, row_bytes, col_bytes, jr, n, i0, w);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          s2::down_batch_fma<T, kWaves>(acc, jr, sr, n, i0, cvalid, w);
+        }
+        s2::down_reduce_add<kFusedThreads, kCw>(red, acc, kEpl, cs, d, y);
+      }
+      __syncthreads();  // jr, sr and red are reused by the next item
     }
   }
-  __syncthreads();
-  if (!s_ok) return;  // gave up: outputs invalid, error word set
 
-  // ---- phase B: the items of this block
-  float* y = a.ug.y;
-  for (int item = blk, first = 1; item < n_items; item += G, first = 0) {
-    if (!first) {
-      cs = item % a.col_slices;
-      c0 = (item / a.col_slices) * a.chan_per_group;
-      const int c1 = min(f, c0 + a.chan_per_group);
-      n = s2::compact_range<kFusedThreads>(s2::range_word(bitmap, c0, c1), c0, c1, jr, s_cnt, slot);
+  // ---- completion ticket: every block adds 1 (plus 1 << 16 if it gave up);
+  // the block that draws the last ticket publishes k_s, or -1 if any block of
+  // this launch gave up, and resets the counter for the next launch.  k_s has
+  // one writer per launch, so a give-up can never be overwritten by it.
+  if (tid == 0) {
+    unsigned* done = reinterpret_cast<unsigned*>(tws + a.off_done);
+    const unsigned mine = 1u + (s_ok ? 0u : 0x10000u);
+    const unsigned prev = __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((prev & 0xFFFFu) == static_cast<unsigned>(G - 1)) {
+      __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ug.mask_count, ((prev + mine) >> 16) != 0u ? -1 : ks, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
-    // s_j of the rows, written by other blocks in phase A
-    if (slot >= 0) sr[slot] = __hip_atomic_load(&ssp[c0 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (n > 0) {  // block-uniform
-      const int col = cs * kCw + lane * kEpl;
-      const bool cvalid = col < d;
-      const int colc = cvalid ? col : cs * kCw;
-      float acc[kEpl];
-#pragma unroll
-      for (int e = 0; e < kEpl; ++e) acc[e] = 0.f;
-      const uint32_t col_bytes = static_cast<uint32_t>(colc * sizeof(S));
-      for (int i0 = wave; i0 < n; i0 += kWaves * kDownUnroll) {
-        if (!first || i0 != wave) {  // the first batch of the first item is already in w
-          s2::down_batch_loads<kWaves>(Wd, row_bytes, col_bytes, jr, n, i0, w);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        s2::down_batch_fma<T, kWaves>(acc, jr, sr, n, i0, cvalid, w);
-      }
-      s2::down_reduce_add<kFusedThreads, kCw>(red, acc, kEpl, cs, d, y);
-    }
-    __syncthreads();  // jr, sr and red are reused by the next item
   }
 }
 

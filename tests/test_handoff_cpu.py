@@ -25,7 +25,10 @@ The opt-in fused Stage-2 kernel joins its two phases with a grid barrier of
 per-block epoch flags and bounded waits; a model of that protocol checks the
 same properties (no block passes before every block's stores are visible,
 flags consistent across launches, including launches whose blocks give up),
-with the same kind of negative control.
+with the same kind of negative control.  Its k_s is published by the block
+that draws the last completion ticket, so a give-up (-1) cannot be overwritten
+by a late k_s; a model checks that too, with the single-writer race it
+replaces as negative control.
 """
 import os
 import random
@@ -264,3 +267,51 @@ def test_grid_barrier_protocol_model_needs_the_wait():
     flags = [0] * 8
     stale = sum(_barrier_call(flags, rng, 10 ** 9, allow_early_flag=True)[0] for _ in range(200))
     assert stale > 0
+
+
+# ---------------------------------------------------------------- fused Stage-2 k_s publication
+def _publish_count(G, gave_up, rng, ticketed=True, done0=0):
+    """Who writes mask_count in one launch of the fused Stage-2 kernel.
+
+    ticketed: every block, at its end, adds 1 (+ 1 << 16 if it gave up) to a
+    completion counter; the block drawing the last ticket writes k_s or -1
+    and resets the counter.  Otherwise (the mistake the model must catch)
+    block 0 writes k_s during its first phase and a block that gives up writes
+    -1 at its wait, both at arbitrary points of the schedule.
+    Returns (final mask_count, final counter)."""
+    ks = 1234
+    mask_count = 77                              # stale value of an earlier launch
+    done = done0
+    if ticketed:
+        for b in rng.sample(range(G), G):        # order in which blocks finish
+            mine = 1 + (0x10000 if b in gave_up else 0)
+            prev = done
+            done += mine
+            if (prev & 0xFFFF) == G - 1:
+                done = 0
+                mask_count = -1 if ((prev + mine) >> 16) else ks
+        return mask_count, done
+    writes = [("ks", 0)] + [("gu", b) for b in gave_up]
+    rng.shuffle(writes)
+    for kind, _ in writes:
+        mask_count = ks if kind == "ks" else -1
+    return mask_count, done
+
+
+def test_fused_count_publication_model():
+    """k_s is -1 exactly when some block of the launch gave up, whatever the
+    finishing order, and the counter is 0 again for the next launch."""
+    rng = random.Random(13)
+    for G in (1, 2, 7, 256):
+        for _ in range(300):
+            gave_up = set(b for b in range(G) if rng.random() < 0.05)
+            mc, done = _publish_count(G, gave_up, rng)
+            assert mc == (-1 if gave_up else 1234) and done == 0
+
+
+def test_fused_count_publication_needs_one_writer():
+    """Negative control: with block 0 writing k_s and give-ups writing -1
+    independently, some schedules end with k_s although a block gave up."""
+    rng = random.Random(17)
+    lost = sum(_publish_count(8, {3, 5}, rng, ticketed=False)[0] != -1 for _ in range(200))
+    assert lost > 0
