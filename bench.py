@@ -956,16 +956,33 @@ def cpu_baseline(rot, taus, args):
 
 
 # ============================================================================ counter runs
+GATHER_TABLE_ROWS = 1 << 21  # 128-byte rows of the gather cross-check table (256 MiB)
+
+
+def gather_reference_rows() -> int:
+    """Rows the gather cross-check selects: every other row on average."""
+    return GATHER_TABLE_ROWS // 2
+
+
 def pmc_copy(n_bytes: int, reps: int) -> None:
     """Device-to-device copies of a known size, the scale reference for the
-    FETCH_SIZE / WRITE_SIZE counters."""
+    FETCH_SIZE / WRITE_SIZE counters; then, as a check that the scale holds
+    for 128-byte gathers like the decode kernels' reads, a torch index_select
+    of a random ascending half of the 128-byte rows of a 256 MiB table."""
     import torch
     src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"copied {n_bytes} bytes {reps} times")
+    del src, dst
+    g = torch.Generator().manual_seed(5)
+    idx = torch.randperm(GATHER_TABLE_ROWS, generator=g)[:gather_reference_rows()].sort().values.to("cuda")
+    table = torch.ones(GATHER_TABLE_ROWS, 64, dtype=torch.bfloat16, device="cuda")
+    for _ in range(reps):
+        out = torch.index_select(table, 0, idx)
+    torch.cuda.synchronize()
+    log(f"copied {n_bytes} bytes {reps} times; gathered {out.shape[0]} rows of 128 bytes {reps} times")
 
 
 def pmc_run(args) -> None:
@@ -1037,6 +1054,19 @@ def summarize_pmc(root: str) -> None:
     write_kib_copy = max(cw[n][0] for n in wname)
     fetch_factor = copy_bytes / (fetch_kib_copy * 1024.0)
     write_factor = copy_bytes / (write_kib_copy * 1024.0)
+    # cross-check of the scale on a 128-byte-row gather of known size
+    gname_f = [n for n in cf if "gather" in n.lower() or "indexselect" in n.lower().replace("_", "")]
+    gname_w = [n for n in cw if "gather" in n.lower() or "indexselect" in n.lower().replace("_", "")]
+    gather_check = None
+    if gname_f and gname_w:
+        n_rows = gather_reference_rows()
+        g_read = n_rows * (128 + 8)   # the rows and their int64 indexes
+        g_write = n_rows * 128
+        gf = max(cf[n][0] for n in gname_f) * 1024.0 * fetch_factor
+        gw = max(cw[n][0] for n in gname_w) * 1024.0 * write_factor
+        gather_check = {"rows": n_rows, "row_bytes": 128, "algorithmic_read": g_read, "algorithmic_write": g_write,
+                        "scaled_fetch": round(gf), "scaled_write": round(gw),
+                        "fetch_ratio": round(gf / g_read, 4), "write_ratio": round(gw / g_write, 4)}
     try:
         with open(TRAFFIC_FILE) as fh:
             store = json.load(fh)
@@ -1045,6 +1075,18 @@ def summarize_pmc(root: str) -> None:
     recs = store.get("records", [])
     lines = [f"Scale: a 1 GiB device copy reads FETCH_SIZE {fetch_kib_copy:.1f} KiB (factor x{fetch_factor:.4f}) "
              f"and WRITE_SIZE {write_kib_copy:.1f} KiB (factor x{write_factor:.4f}).", ""]
+    lines += ["Check of the FETCH_SIZE scale on this library's own loads: every algorithmic byte a kernel does "
+              "not write must be fetched at least once, so (algorithmic - written) / raw FETCH bytes is the "
+              "smallest factor consistent with each launch (last column below).  A lower bound near the copy's "
+              "factor (the contiguous 16 KB up/gate runs) pins the factor for these loads; a bound above it "
+              "would expose an undercount.", ""]
+    if gather_check:
+        lines += [f"The scale depends on the request type: torch's index_select of {gather_check['rows']} rows of "
+                  f"128 bytes (ascending random half of a 256 MiB table) reads raw FETCH_SIZE "
+                  f"{gather_check['scaled_fetch'] / fetch_factor / 1e6:.2f} MB for {gather_check['algorithmic_read'] / 1e6:.2f} MB "
+                  f"of rows and indexes, x{gather_check['fetch_ratio']:.3f} after the copy's factor (either that kernel "
+                  f"fetches twice its bytes or its requests count at full size); its writes scale to "
+                  f"x{gather_check['write_ratio']:.3f}.", ""]
     for meta_path in sorted(glob.glob(os.path.join(root, "*_meta.json"))):
         tag = os.path.basename(meta_path)[:-len("_meta.json")]
         with open(meta_path) as fh:
@@ -1053,8 +1095,9 @@ def summarize_pmc(root: str) -> None:
         wm = _counter_means(os.path.join(root, tag + "_write"), "WRITE_SIZE")
         key = meta["key"]
         lines += [f"### {tag}: {key}", "",
-                  "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
-                  "|---|---|---|---|---|---|---|"]
+                  "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio "
+                  "| FETCH factor lower bound |",
+                  "|---|---|---|---|---|---|---|---|"]
         for kernel, alg in meta["algorithmic_bytes_per_launch"].items():
             pats = KERNELS[kernel][1]
             f_kib = sum(v[0] for n, v in fm.items() if any(p in n for p in pats))
@@ -1064,15 +1107,20 @@ def summarize_pmc(root: str) -> None:
                 continue
             fb = f_kib * 1024.0 * fetch_factor
             wb = w_kib * 1024.0 * write_factor
+            # every algorithmic byte that is not written must be fetched at least once:
+            # the smallest FETCH_SIZE factor consistent with this launch's raw count
+            f_lb = (alg - wb) / (f_kib * 1024.0) if f_kib > 0 else None
             rec = {"kernel": kernel, **key, "source_sha256": meta["source_sha256"][kernel],
                    "dispatches": n_disp, "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
                    "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
                    "hbm_bytes_per_launch": round(fb + wb), "algorithmic_bytes_per_launch": round(alg),
-                   "ratio_to_algorithmic": round((fb + wb) / alg, 3)}
+                   "ratio_to_algorithmic": round((fb + wb) / alg, 3),
+                   "fetch_factor_lower_bound": None if f_lb is None else round(f_lb, 4)}
             recs = [r for r in recs if not (r.get("kernel") == kernel and all(r.get(k) == v for k, v in key.items()))]
             recs.append(rec)
             lines.append(f"| {kernel} | {n_disp} | {f_kib:.1f} | {w_kib:.1f} | {(fb + wb) / 1e6:.2f} MB | "
-                         f"{alg / 1e6:.2f} MB | {(fb + wb) / alg:.3f} |")
+                         f"{alg / 1e6:.2f} MB | {(fb + wb) / alg:.3f} | "
+                         f"{'-' if f_lb is None else f'{f_lb:.3f}'} |")
         lines.append("")
     store = {"_about": "HBM bytes per launch of the decode kernels from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE "
                        "runs (KiB per dispatch, mean over the dispatches of one pass over a workload's rotation), "
@@ -1081,7 +1129,7 @@ def summarize_pmc(root: str) -> None:
                        "prox_internal.h, and bench.py reports a record only while it matches.",
              "scale": {"copy_bytes": copy_bytes, "fetch_kib_read": round(fetch_kib_copy, 1),
                        "write_kib_read": round(write_kib_copy, 1), "fetch_factor": fetch_factor,
-                       "write_factor": write_factor},
+                       "write_factor": write_factor, "gather128_check": gather_check},
              "records": recs}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(store, fh, indent=1)
