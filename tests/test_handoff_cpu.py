@@ -25,7 +25,10 @@ The opt-in fused Stage-2 kernel joins its two phases with a grid barrier of
 per-block epoch flags and bounded waits; a model of that protocol checks the
 same properties (no block passes before every block's stores are visible,
 flags consistent across launches, including launches whose blocks give up),
-with the same kind of negative control.  Its k_s is published by the block
+with the same kind of negative control, and its generated code is checked for
+the arrival sequence the protocol assumes (phase-A stores complete, first
+W_down batch still in flight, block barrier, then the flag).  Its k_s is
+published by the block
 that draws the last completion ticket, so a give-up (-1) cannot be overwritten
 by a late k_s; a model checks that too, with the single-writer race it
 replaces as negative control.
@@ -315,3 +318,66 @@ def test_fused_count_publication_needs_one_writer():
     rng = random.Random(17)
     lost = sum(_publish_count(8, {3, 5}, rng, ticketed=False)[0] != -1 for _ in range(200))
     assert lost > 0
+
+
+# ---------------------------------------------------------------- fused Stage-2 barrier arrival
+def _kernel_lines(asm: str, name_part: str):
+    """{symbol: [instruction or label lines]} (labels kept, comments dropped)."""
+    bodies, cur = {}, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            cur = [] if name_part in m.group(1) else None
+            if cur is not None:
+                bodies[m.group(1)] = cur
+            continue
+        if cur is None:
+            continue
+        ins = line.split(";")[0].strip()
+        if not ins or ins.startswith("."):
+            if ins.startswith(".LBB"):
+                cur.append(ins)
+            continue
+        cur.append(ins)
+        if ins.startswith("s_endpgm"):
+            cur = None
+    return bodies
+
+
+def _down_unroll() -> int:
+    with open(os.path.join(CSRC, "prox_internal.h")) as fh:
+        return int(re.search(r"constexpr int kDownUnroll = (\d+);", fh.read()).group(1))
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_fused_barrier_arrival_in_generated_code(tmp_path):
+    """The fused Stage-2 kernel arrives at its grid barrier only after its
+    phase-A stores are complete, without waiting for the first W_down batch:
+    the last kDownUnroll vector-memory instructions before its
+    s_waitcnt vmcnt(kDownUnroll) are those loads, in straight-line code (no
+    label between them and the wait), and the wait is followed by the block
+    barrier and then the device-coherent flag store.  A store moved into the
+    window, or a branch, would let a block publish its flag early."""
+    k = _down_unroll()
+    bodies = _kernel_lines(_device_asm("stage2_fused.hip", tmp_path), "stage2_fused_kernel")
+    assert len(bodies) == 2, f"expected the bf16 and fp32 kernels, found {list(bodies)}"
+    for sym, ins in bodies.items():
+        waits = [i for i, s in enumerate(ins) if s == f"s_waitcnt vmcnt({k})"
+                 and any(t.startswith("s_barrier") for t in ins[i + 1:i + 3])]
+        arrivals = []
+        for w in waits:
+            after = ins[w + 1:w + 20]
+            b = next(j for j, t in enumerate(after) if t.startswith("s_barrier"))
+            st = [j for j, t in enumerate(after) if t.startswith("global_store") and re.search(r"\bsc1\b", t)]
+            if st and st[0] > b:
+                arrivals.append(w)
+        assert len(arrivals) == 1, f"{sym}: expected one barrier arrival, found {len(arrivals)}"
+        w = arrivals[0]
+        vmem = [i for i in range(w) if ins[i].startswith(("global_", "buffer_", "flat_", "scratch_"))]
+        last = vmem[-k:]
+        assert all(ins[i].startswith("global_load_dwordx4") for i in last), \
+            f"{sym}: the {k} operations before the arrival wait are not all W_down loads"
+        assert not any(t.startswith(".LBB") or t.startswith("s_cbranch") or t.startswith("s_branch")
+                       for t in ins[last[0]:w]), f"{sym}: control flow between the W_down loads and the wait"
+        assert not any(ins[i].startswith(("global_store", "global_atomic", "buffer_store", "scratch_store"))
+                       for i in range(last[0], w)), f"{sym}: a store inside the window"
