@@ -1075,7 +1075,10 @@ PROX_API prox_status prox_ffn_decode_noalloc(const prox_layer* layer, const void
     hipStream_t s = static_cast<hipStream_t>(stream);
     // Every completed call leaves its tickets at zero; another shape moves the
     // token slices (and their tickets) onto bytes that held other data, and a
-    // larger batch reaches slices not used before: clear the region then.
+    // larger batch reaches slices not used before: clear the region then.  The
+    // slice size and offsets make_plan computes depend on d_model and d_ff
+    // only (no term in the weight type or proxy kind), so those and the batch
+    // are the key.
     // (A fill kernel, not a memset, so a captured call replays correctly.)
     if (sc.d != layer->d_model || sc.f != layer->d_ff || batch > sc.batch) {
       e = launch_fill_zero(sc.ptr, need, s);
