@@ -276,6 +276,11 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   // split loads go out in groups of 8 so they travel together; the sums keep
   // the fixed split order
   float* sv = red;  // every thread finished reading red before the ticket barrier
+  // k_x: wave 0 of panel 0's last block reads the split counts (stored before
+  // the ticket like the partials, one per lane: splits <= 64) right after its
+  // first partial loads, so both travel in one round trip
+  const bool count_kx = panel == 0 && a.in_count != nullptr && wave == 0;  // wave-uniform
+  int kc = 0;
   if (has_out) {
     float tot = 0.f;
     for (int k0 = 0; k0 < a.splits; k0 += 8) {
@@ -286,6 +291,8 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
         pv[u] = __hip_atomic_load(&partial[(static_cast<size_t>(kk) * 2 + mo) * f + col], __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
       }
+      if (k0 == 0 && count_kx)
+        kc = __hip_atomic_load(&kcount[min(lane, a.splits - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (k0 + u < a.splits) tot += pv[u];
@@ -308,13 +315,8 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   }
   // ready for the next stream-ordered call
   if (tid == 0) __hip_atomic_store(&tickets[panel], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (panel == 0 && a.in_count != nullptr && wave == 0) {
-    // k_x: one split count per lane (splits <= 64), summed across the wave,
-    // so the loads make one round trip
-    const int kc = lane < a.splits
-                       ? __hip_atomic_load(&kcount[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                       : 0;
-    const int t = wave_sum_int(kc);
+  if (count_kx) {
+    const int t = wave_sum_int(lane < a.splits ? kc : 0);
     if (lane == 0) a.in_count[b] = t;
   }
 }

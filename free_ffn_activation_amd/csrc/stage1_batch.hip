@@ -369,6 +369,15 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(3))
   const int o = tid;
   const int mm = o / kPw;  // 0 = up, 1 = gate
   const size_t ocol = static_cast<size_t>(panel) * kPw + (o % kPw);
+  // k_x: wave 0 of panel 0's last block (lane t: token t) reads the first 8
+  // split counts (stored before the ticket like the partials) right after its
+  // first partial loads, so both travel in one round trip
+  const bool count_kx = panel == 0 && a.in_count != nullptr && wave == 0;  // wave-uniform
+  const int* kcount = reinterpret_cast<const int*>(a.ws + static_cast<size_t>(min(lane, nt - 1)) * a.tok_bytes +
+                                                   a.off_kcount);
+  int kv0[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) kv0[u] = 0;
   float tot[kBatchMax];
 #pragma unroll
   for (int t = 0; t < kBatchMax; ++t) tot[t] = 0.f;
@@ -384,6 +393,11 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(3))
         pv[t][u] = __hip_atomic_load(&partial[(static_cast<size_t>(kk) * 2 + mm) * f + ocol], __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
       }
+    }
+    if (k0 == 0 && count_kx) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        kv0[u] = __hip_atomic_load(&kcount[min(u, a.splits - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
     for (int t = 0; t < kBatchMax; ++t)
@@ -415,21 +429,21 @@ __global__ __launch_bounds__(kS1bThreads) __attribute__((amdgpu_waves_per_eu(3))
     }
   }
   if (tid == 0) __hip_atomic_store(&tickets[panel], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (panel == 0 && a.in_count != nullptr && tid < nt) {
-    // thread t adds token t's per-split counts; each batch of 8 loads is in
-    // flight together
-    const int* kcount = reinterpret_cast<const int*>(a.ws + static_cast<size_t>(tid) * a.tok_bytes + a.off_kcount);
-    int s = 0;
-    for (int k0 = 0; k0 < a.splits; k0 += 8) {
+  if (count_kx && lane < nt) {
+    int kx_sum = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < a.splits) kx_sum += kv0[u];
+    for (int k0 = 8; k0 < a.splits; k0 += 8) {  // more than 8 splits (narrow layers)
       int kv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         kv[u] = __hip_atomic_load(&kcount[min(k0 + u, a.splits - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (k0 + u < a.splits) s += kv[u];
+        if (k0 + u < a.splits) kx_sum += kv[u];
     }
-    a.in_count[tid] = s;
+    a.in_count[lane] = kx_sum;
   }
 }
 

@@ -166,6 +166,11 @@ __global__ __launch_bounds__(kThreads) void stage1_w16_kernel(Stage1Args a) {
   if (!s_last) return;
 
   float* sv = red;  // every thread finished reading red before the ticket barrier
+  // k_x: wave 0 of panel 0's last block reads the split counts (stored before
+  // the ticket like the partials, one per lane: splits <= 64) right after its
+  // first partial loads, so both travel in one round trip
+  const bool count_kx = panel == 0 && a.in_count != nullptr && wave == 0;  // wave-uniform
+  int kc = 0;
   float tot = 0.f;
   for (int k0 = 0; k0 < a.splits; k0 += 8) {
     float pv[8];
@@ -173,6 +178,8 @@ __global__ __launch_bounds__(kThreads) void stage1_w16_kernel(Stage1Args a) {
     for (int u = 0; u < 8; ++u)
       pv[u] = __hip_atomic_load(&partial[(static_cast<size_t>(min(k0 + u, a.splits - 1)) * 2 + m) * f + col],
                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (k0 == 0 && count_kx)
+      kc = __hip_atomic_load(&kcount[min(lane, a.splits - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (k0 + u < a.splits) tot += pv[u];
@@ -190,21 +197,10 @@ __global__ __launch_bounds__(kThreads) void stage1_w16_kernel(Stage1Args a) {
       bitmap[w0 + 1] = static_cast<uint32_t>(bal >> 32);
     }
   }
-  if (tid == 0) {
-    __hip_atomic_store(&tickets[panel], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (panel == 0 && a.in_count != nullptr) {
-      int s = 0;
-      for (int k0 = 0; k0 < a.splits; k0 += 8) {
-        int kv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          kv[u] = __hip_atomic_load(&kcount[min(k0 + u, a.splits - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (k0 + u < a.splits) s += kv[u];
-      }
-      a.in_count[b] = s;
-    }
+  if (tid == 0) __hip_atomic_store(&tickets[panel], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (count_kx) {
+    const int t = wave_sum_int(lane < a.splits ? kc : 0);
+    if (lane == 0) a.in_count[b] = t;
   }
 }
 
