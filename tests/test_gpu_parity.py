@@ -270,6 +270,34 @@ def test_decode_max_d_model(P):
     _run_decode(P, L, layer, ov, [1, 2, 3], tau_x, tau_s, "12288x256-b3")
 
 
+def test_decode_max_d_ff(P):
+    """d_ff = 65536, the largest: four 16384-channel bitmap chunks (two held
+    in registers by every up/gate wave, two re-read), 512 Stage-1 panels, the
+    grouped kernels' union scan over 2048 words in 8 passes; batch 1, a
+    grouped batch of 3 and the all-pass case."""
+    layer = synth.make_layer(_small_cfg(128, 65536, "bf16", 47), n_dec=4)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov)
+    _run_decode(P, L, layer, ov, [0], tau_x, tau_s, "128x65536")
+    _run_decode(P, L, layer, ov, [1, 2, 3], tau_x, tau_s, "128x65536-b3")
+    y, mi, mc, ic = _run_decode(P, L, layer, ov, [2], 0.0, 0.0, "128x65536-all-pass")
+    assert mc[0] == L.d_ff and np.array_equal(mi[0], np.arange(L.d_ff))
+
+
+def test_decode_max_d_model_f32(P):
+    """d_model = 12288 with fp32 weights: x staged by the up/gate kernel takes
+    48 KB of LDS and the down kernel's column slices are 256 wide (48 of
+    them); batch 1 and two tokens (per-token kernels: fp32 groups run Stage 2
+    per token)."""
+    layer = synth.make_layer(_small_cfg(12288, 256, "f32", 48), n_dec=3)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov)
+    _run_decode(P, L, layer, ov, [0], tau_x, tau_s, "12288x256-f32")
+    _run_decode(P, L, layer, ov, [1, 2], tau_x, tau_s, "12288x256-f32-b2")
+
+
 def test_decode_degenerate_thresholds(P):
     layer, ov = oracle_layer("tiny")
     L = pack_layer(layer)
