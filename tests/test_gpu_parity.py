@@ -660,11 +660,12 @@ def test_fused_and_split_stage2_agree(P, layer8b):
 
 
 @pytest.mark.parametrize("d,f,dt,seed", [(256, 768, "f32", 101), (320, 384, "bf16", 41), (12288, 256, "bf16", 46),
-                                         (128, 33024, "bf16", 45)])
+                                         (12288, 256, "f32", 48), (128, 33024, "bf16", 45),
+                                         (128, 65536, "bf16", 47)])
 def test_fused_stage2_parity_shapes(P, d, f, dt, seed):
     """The fused Stage-2 kernel against the oracle on fp32, a partial column
-    slice, the largest d_model and a three-chunk bitmap, plus the degenerate
-    thresholds (all-pass, empty mask)."""
+    slice, the largest d_model (bf16 and fp32), a three-chunk bitmap and the
+    largest d_ff, plus the degenerate thresholds (all-pass, empty mask)."""
     layer = synth.make_layer(_small_cfg(d, f, dt, seed), n_dec=3)
     ov = oracle_view(layer)
     L = pack_layer(layer)
