@@ -1167,7 +1167,7 @@ def main() -> int:
     log(f"headline: {head['us_per_layer']:.2f} us/layer, {head['required_MB_per_layer']:.2f} MB required, "
         f"{head['achieved_GBps']:.0f} GB/s ({head['pct_hbm_roofline']:.1f}% of 8 TB/s)")
 
-    # box streaming context
+    # streaming-copy context on this GPU
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -1238,7 +1238,7 @@ def main() -> int:
         "mean_k_s": head["mean_k_s"],
         "eager_us_per_layer": head["eager_us_per_layer"],
         "step_us": head["step_us"],
-        "box_copy_GBps_read_plus_write": round(copy_gbps, 1),
+        "device_copy_GBps_read_plus_write": round(copy_gbps, 1),
         "kernels": head.get("kernels"),
         "dense_us_per_layer": head.get("dense_us_per_layer"),
         "roofline": head.get("roofline"),

@@ -21,9 +21,9 @@
 //     channel range, read from the Stage-1 bitmap.  Each block compacts its
 //     first item's rows and issues its first batch of W_down loads *before* the
 //     grid barrier: the down weight stream overlaps the barrier and the other
-//     blocks' up/gate tail, and only the s_j values wait.  (Measured on this
-//     box: a kernel boundary costs 1.6 us, an in-kernel grid barrier 2.8 us;
-//     the barrier pays only because it hides behind those loads.)
+//     blocks' up/gate tail, and only the s_j values wait.  (Measured on
+//     MI355X: a kernel boundary costs 1.6 us, an in-kernel grid barrier 2.8 us;
+//     the barrier pays only if it hides behind those loads.)
 //   * ordering: gfx9-family hardware retires vector memory operations in
 //     issue order on one counter (vmcnt), so after issuing its W_down loads a
 //     thread waits with vmcnt(kDownUnroll) — its phase-A stores are then
