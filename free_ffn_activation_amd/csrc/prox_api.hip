@@ -241,15 +241,16 @@ std::atomic<uint32_t> g_wait_ticks{kDefaultWaitTicks};
 // CU for each (weight dtype, LDS bytes) seen.
 struct DevInfo {
   int cus = 0;
+  int coop = -1;  // hipDeviceAttributeCooperativeLaunch
   std::vector<std::pair<std::pair<int, size_t>, int>> occ;
 };
 std::mutex g_dev_mu;
 std::vector<DevInfo> g_dev;
 
 // Grid of the fused Stage-2 kernel on the current device (one block per CU),
-// or 0 when it cannot run there: fewer than one resident block per CU, more
-// CUs than the workspace holds barrier flags for, or a failed query (the two
-// Stage-2 kernels run instead).
+// or 0 when it cannot run there: no cooperative launches, fewer than one
+// resident block per CU, more CUs than the workspace holds barrier flags for,
+// or a failed query (the two Stage-2 kernels run instead).
 int fused_grid(int wdtype, size_t smem) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
@@ -260,6 +261,11 @@ int fused_grid(int wdtype, size_t smem) {
     di.cus = 0;
     return 0;
   }
+  if (di.coop < 0 && hipDeviceGetAttribute(&di.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) {
+    di.coop = -1;
+    return 0;
+  }
+  if (di.coop != 1) return 0;
   int occ = -1;
   for (const auto& e : di.occ)
     if (e.first.first == wdtype && e.first.second == smem) occ = e.second;
@@ -360,8 +366,14 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
   }
   if (fgrid > 0) {
     e = launch_stage2_fused(fa, layer->wdtype, fgrid, s);
-    if (e != hipSuccess) return hip_fail(e, "fused stage-2 launch");
-  } else if (stages & PROX_STAGE_UPGATE) {
+    if (e == hipErrorCooperativeLaunchTooLarge) {  // the runtime cannot hold the grid now: two kernels
+      (void)hipGetLastError();
+      fgrid = 0;
+    } else if (e != hipSuccess) {
+      return hip_fail(e, "fused stage-2 launch");
+    }
+  }
+  if (fgrid == 0 && (stages & PROX_STAGE_UPGATE)) {
     if (!any2) {
       e = launch_upgate(upgate_args(p, layer, x, ws, mask_idx, mask_count, y), layer->wdtype, batch,
                         p.ug_blocks, true, s);

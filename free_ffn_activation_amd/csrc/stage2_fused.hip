@@ -10,9 +10,10 @@
 // Stage 2 starts; only the values s_j are produced inside Stage 2.
 //
 // gfx950 design:
-//   * one block of 1024 threads per CU: grid = the CU count, every block
-//     resident at once (the host checks the occupancy, and every wait below is
-//     bounded).  16 waves per block, 4 per SIMD.
+//   * one block of 1024 threads per CU: grid = the CU count, launched
+//     cooperatively so that every block is resident at once (the host also
+//     checks the occupancy first, and every wait below is bounded).  16 waves
+//     per block, 4 per SIMD.
 //   * phase A is the up/gate kernel's work (s2::upgate_block) over all the
 //     grid's waves: s_j by channel index, the ascending index list, k_s, and
 //     the zeros of y, all written with agent-coherent stores.
@@ -197,15 +198,17 @@ hipError_t fused_occupancy(int wdtype, size_t smem, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, stage2_fused_kernel<F32Tag>, kFusedThreads, smem);
 }
 
+// A cooperative launch: the runtime starts it only with every block resident
+// at once (or refuses it with hipErrorCooperativeLaunchTooLarge), which is
+// what the grid barrier needs; the bounded waits remain as a second guard.
 hipError_t launch_stage2_fused(const FusedArgs& a, int wdtype, int grid, hipStream_t s) {
   const size_t smem = fused_smem(a);
-  if (wdtype == PROX_BF16)
-    hipLaunchKernelGGL(stage2_fused_kernel<Bf16Tag>, dim3(static_cast<unsigned>(grid)), dim3(kFusedThreads), smem, s,
-                       a);
-  else
-    hipLaunchKernelGGL(stage2_fused_kernel<F32Tag>, dim3(static_cast<unsigned>(grid)), dim3(kFusedThreads), smem, s,
-                       a);
-  return hipGetLastError();
+  FusedArgs args = a;
+  void* params[] = {&args};
+  const void* fn = wdtype == PROX_BF16 ? reinterpret_cast<const void*>(stage2_fused_kernel<Bf16Tag>)
+                                       : reinterpret_cast<const void*>(stage2_fused_kernel<F32Tag>);
+  return hipLaunchCooperativeKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(kFusedThreads), params,
+                                    static_cast<unsigned>(smem), s);
 }
 
 }  // namespace prox

@@ -331,11 +331,12 @@ prox_status prox_ffn_decode_events(const prox_layer* layer, const void* x, int32
  * Stage-1 mask, before it waits).  Same results up to the fp32 order of the
  * atomic additions into y.  Measured slower than the two launches on MI355X
  * (device-coherent stores and polls are slow while the weight stream holds the
- * memory system); kept for comparison.  Where the device cannot hold the grid
- * the two kernels run instead.  The barrier's wait is bounded
- * (prox_set_wait_limit): a call whose blocks were not all resident in time
- * (another kernel holding the GPU) sets mask_count[0] = -1 and the workspace
- * error word (prox_workspace_check) and leaves y undefined. */
+ * memory system); kept for comparison.  It is a cooperative launch (the
+ * runtime starts it with every block resident at once); where the device has
+ * no cooperative launches or cannot hold the grid, the two kernels run
+ * instead.  The barrier's wait is also bounded (prox_set_wait_limit): a call
+ * whose blocks did not all arrive in time sets mask_count[0] = -1 and the
+ * workspace error word (prox_workspace_check) and leaves y undefined. */
 #define PROX_STAGE_FUSED_STAGE2 32
 prox_status prox_ffn_decode_stages(const prox_layer* layer, const void* x, int32_t batch,
                                    float tau_x, float tau_s, float* y, int32_t* mask_idx,
