@@ -15,7 +15,10 @@ Method of measurement
     overhead); the eager rate is reported beside it.
   * Each kernel is also replayed alone over the same steps (HIP events on the
     stream the kernels run on); the dominant kernel's algorithmic bytes over
-    its mean duration is the roofline figure.
+    its mean duration is the roofline figure.  The opt-in fused Stage-2
+    kernel (a cooperative launch) is timed beside them unless --no-fused
+    (kernel-trace runs use it: rocprofv3 loses its trace output after
+    cooperative launches).
   * Required bytes use the actual k_x and k_s of each timed step, averaged
     over exactly the K timed steps:
     k_x*d_ff (INT4 up+gate rows) + 8*k_x (scales) + 3*k_s*d_model*2 (kept bf16
@@ -132,6 +135,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="leave out the opt-in fused Stage-2 timings (kernel-trace runs: rocprofv3 loses its "
+                         "trace output after the kernel's cooperative launches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-budget", action="store_true",
                     help="skip the computation-budget, calibration, 16-bit proxy and GeGLU sections")
@@ -391,11 +397,12 @@ def measure_decode(rot, taus, K: int, workload: str, keep_x: float, sparsity_s: 
         # PROX_STAGE_FUSED_STAGE2) for comparison
         fused = prox.PROX_STAGE_FUSED_STAGE2
         runs = [("stage1_proxy", prox.PROX_STAGE_PROXY), ("stage2_upgate", prox.PROX_STAGE_UPGATE),
-                ("stage2_down", prox.PROX_STAGE_DOWN),
-                ("stage2_fused", prox.PROX_STAGE_UPGATE | prox.PROX_STAGE_DOWN | fused)]
+                ("stage2_down", prox.PROX_STAGE_DOWN)]
+        if not args.no_fused:
+            runs.append(("stage2_fused", prox.PROX_STAGE_UPGATE | prox.PROX_STAGE_DOWN | fused))
         k_us = {nm: time_graph(staged(b), spr, K, f"{workload} {nm} alone", graph=not args.no_graph)
                 for nm, b in runs}
-        if not args.no_graph:
+        if not args.no_graph and not args.no_fused:
             res["us_per_layer_fused_stage2"] = round(
                 time_graph(staged(7 | fused), spr, K, f"{workload} decode, Stage 2 fused (opt-in)"), 3)
         del iso
