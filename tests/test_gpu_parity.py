@@ -298,6 +298,36 @@ def test_decode_max_d_model_f32(P):
     _run_decode(P, L, layer, ov, [1, 2], tau_x, tau_s, "12288x256-f32-b2")
 
 
+def _sweep_cases(n=12, seed=2027):
+    """Seeded draws of valid layers and operating points: d_model a multiple of
+    64 up to 2048, d_ff a multiple of 128 up to 6144, bf16 or fp32, 1 to 9
+    tokens (so groups of 1, 2, 3.. 8 and 8 + 1 all occur), keep_x and s2 off
+    the headline point."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = 64 * int(rng.integers(1, 33))
+        f = 128 * int(rng.integers(1, 49))
+        dt = "bf16" if rng.random() < 0.7 else "f32"
+        b = int(rng.integers(1, 10))
+        keep_x = float(rng.choice([0.2, 0.3, 0.5, 0.8]))
+        s2 = float(rng.choice([0.4, 0.5, 0.7, 0.9]))
+        cases.append((d, f, dt, b, keep_x, s2, 300 + i))
+    return cases
+
+
+@pytest.mark.parametrize("d,f,dt,b,keep_x,s2,seed", _sweep_cases())
+def test_decode_seeded_shape_sweep(P, d, f, dt, b, keep_x, s2, seed):
+    """Decode parity on seeded random shapes, dtypes, batch sizes and
+    operating points (default dispatch: per-token or grouped kernels by group
+    size), every token against the oracle under the band rule."""
+    layer = synth.make_layer(_small_cfg(d, f, dt, seed), n_dec=b)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov, keep_x=keep_x, sparsity_s=s2)
+    _run_decode(P, L, layer, ov, list(range(b)), tau_x, tau_s, f"{d}x{f}-{dt}-b{b}-k{keep_x}-s{s2}")
+
+
 def test_decode_degenerate_thresholds(P):
     layer, ov = oracle_layer("tiny")
     L = pack_layer(layer)
