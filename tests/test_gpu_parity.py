@@ -328,6 +328,16 @@ def test_decode_seeded_shape_sweep(P, d, f, dt, b, keep_x, s2, seed):
     _run_decode(P, L, layer, ov, list(range(b)), tau_x, tau_s, f"{d}x{f}-{dt}-b{b}-k{keep_x}-s{s2}")
 
 
+@pytest.mark.parametrize("d,f,dt,b,keep_x,s2,seed", _sweep_cases(n=4, seed=2029))
+def test_geglu_decode_seeded_shape_sweep(P, d, f, dt, b, keep_x, s2, seed):
+    """The seeded sweep for GeGLU layers (GELU-tanh gate)."""
+    layer = synth.make_layer(_small_cfg(d, f, dt, seed), n_dec=b)
+    ov = oracle_view(layer)
+    L = pack_layer(layer, activation=P.PROX_ACT_GELU_TANH)
+    tau_x, tau_s = _oracle_taus(ov, keep_x=keep_x, sparsity_s=s2, act=GELU)
+    _run_decode(P, L, layer, ov, list(range(b)), tau_x, tau_s, f"geglu {d}x{f}-{dt}-b{b}", act=GELU)
+
+
 def test_decode_degenerate_thresholds(P):
     layer, ov = oracle_layer("tiny")
     L = pack_layer(layer)

@@ -144,3 +144,27 @@ def test_proxy16_minimum_shape_and_degenerate(P):
     assert mc[0] == 128
     mi, mc = _decode_check(P, L16, layer, ov, [1], math.inf, 1e-6, "w16-nothing")
     assert mc[0] == 0
+
+
+def _sweep16(n=4, seed=2031):
+    """Seeded bf16 layers and operating points for the 16-bit proxy: d_model a
+    multiple of 64 up to 2048, d_ff a multiple of 128 up to 6144, 1 to 9
+    tokens, keep_x and s2 off the headline point."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        out.append((64 * int(rng.integers(1, 33)), 128 * int(rng.integers(1, 49)), int(rng.integers(1, 10)),
+                    float(rng.choice([0.2, 0.3, 0.5, 0.8])), float(rng.choice([0.4, 0.5, 0.7, 0.9])), 400 + i))
+    return out
+
+
+@pytest.mark.parametrize("d,f,b,keep_x,s2,seed", _sweep16())
+def test_proxy16_decode_seeded_shape_sweep(P, d, f, b, keep_x, s2, seed):
+    """Decode with the 16-bit proxy on seeded random shapes, batch sizes and
+    operating points, thresholds from the oracle's 16-bit calibration."""
+    layer = synth.make_layer(_cfg(d, f, seed, b), n_dec=b)
+    ov = oracle_view(layer)
+    _L, L16 = _pack16(P, layer)
+    Wu, Wg = _ov16(ov)
+    tau_x, tau_s = oracle.calibrate_w16(ov["x_cal"], Wu, Wg, keep_x, s2)
+    _decode_check(P, L16, layer, ov, list(range(b)), tau_x, tau_s, f"w16 {d}x{f}-b{b}-k{keep_x}-s{s2}")
