@@ -718,6 +718,18 @@ def test_fused_stage2_parity_shapes(P, d, f, dt, seed):
     assert mc[0] == 0 and np.all(y == 0)
 
 
+@pytest.mark.parametrize("d,f,dt,b,keep_x,s2,seed", _sweep_cases(n=4, seed=2033))
+def test_fused_stage2_seeded_shape_sweep(P, d, f, dt, b, keep_x, s2, seed):
+    """The fused Stage-2 kernel on seeded random shapes, dtypes and operating
+    points, against the oracle (the kernel serves batch 1: each draw's batch
+    size is not used)."""
+    layer = synth.make_layer(_small_cfg(d, f, dt, seed), n_dec=1)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    tau_x, tau_s = _oracle_taus(ov, keep_x=keep_x, sparsity_s=s2)
+    _run_decode(P, L, layer, ov, [0], tau_x, tau_s, f"fused {d}x{f}-{dt}", stages=7 | P.PROX_STAGE_FUSED_STAGE2)
+
+
 def test_fused_stage2_items_beyond_the_grid(P):
     """d_model 12288 x d_ff 11264 (bf16): 24 column slices x 11 row groups =
     264 down items for a 256-block grid, so some blocks of the fused Stage-2
