@@ -442,6 +442,38 @@ def test_calibrate_parity(P, name, n_tok):
     assert math.isinf(tx1) and math.isinf(ts1)
 
 
+def _calib_cases(n=8, seed=2035):
+    """Seeded layers, calibration-set sizes and keep fractions (n_keep at
+    both ends of the range and off round numbers of the fp32 keep value)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = 64 * int(rng.integers(1, 33))
+        f = 128 * int(rng.integers(1, 49))
+        dt = "bf16" if rng.random() < 0.6 else "f32"
+        n_tok = int(rng.integers(1, 25))
+        keep_x = float(rng.choice([0.01, 0.1, 0.3, 0.37, 0.5, 0.9, 0.99]))
+        s2 = float(rng.choice([0.05, 0.3, 0.7, 0.85, 0.97]))
+        out.append((d, f, dt, n_tok, keep_x, s2, 500 + i))
+    return out
+
+
+@pytest.mark.parametrize("d,f,dt,n_tok,keep_x,s2,seed", _calib_cases())
+def test_calibrate_seeded_sweep(P, d, f, dt, n_tok, keep_x, s2, seed):
+    """prox_calibrate on seeded shapes, calibration-set sizes (1 to 24
+    tokens) and keep fractions from 1% to 99%: tau_x bit-exact and tau_s
+    within 1e-5 relative of the oracle's order statistics."""
+    layer = synth.make_layer(_small_cfg(d, f, dt, seed), n_dec=1, n_cal=24)
+    ov = oracle_view(layer)
+    L = pack_layer(layer)
+    xc = to_device(layer.x_cal[:n_tok], dt)
+    ws = torch.empty(P.prox_calibrate_workspace_size(d, f, n_tok), dtype=torch.uint8, device="cuda")
+    tx, ts = P.prox_calibrate(L, xc, keep_x, s2, ws)
+    rx, rs = _oracle_taus(ov, keep_x, s2, n_tok=n_tok)
+    assert np.float32(tx) == np.float32(rx), f"tau_x {tx!r} vs {rx!r}"
+    assert abs(ts - rs) <= 1e-5 * abs(rs), f"tau_s {ts!r} vs {rs!r}"
+
+
 # ------------------------------------------------------------------ graph replay
 @pytest.mark.parametrize("name", ["tiny", "qwen3_8b"])
 def test_graph_replay_matches_eager(P, name):
