@@ -23,6 +23,7 @@ constexpr int kFusedItems = 256;       // fused Stage-2 kernel: down items plann
 constexpr int kMaxGridFlags = 1024;    // fused Stage-2 kernel: grid-barrier flags in the workspace
 constexpr uint32_t kDefaultWaitTicks = 4000000u;  // bounded waits: 40 ms of the 100 MHz real-time clock
 constexpr int kBatchMax = 8;           // tokens per group of the batched kernels
+constexpr int kS1MaxRowsPerSplit = 896;  // Stage 1: input rows per K-split at most (one gather batch per wave)
 constexpr int kGroupedMinTokens = 3;   // smaller groups run the per-token kernels (faster there)
 
 // ---------------------------------------------------------------------------

@@ -278,7 +278,7 @@ prox_status prox_ffn_decode(const prox_layer* layer, const void* x, int32_t batc
  *   - prox_workspace_size(d_model, d_ff, batch) must not exceed
  *     PROX_NOALLOC_SCRATCH_BYTES, else PROX_ERR_UNSUPPORTED and nothing is
  *     enqueued (32 MiB holds, e.g., 18 tokens of the Qwen3-8B-shaped layer
- *     and 14 of the Qwen3-32B-shaped one).
+ *     and 12 of the Qwen3-32B-shaped one).
  *   - The first call on a GPU, and a call whose shape differs from the
  *     previous call's on that GPU or whose batch exceeds every earlier one,
  *     also enqueues a fill kernel that clears the used part of the array.
