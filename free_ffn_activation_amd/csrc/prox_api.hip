@@ -574,11 +574,14 @@ Plan make_plan(int d, int f, int wdtype) {
     const int wpb = kUgThreads / 64;
     p.ug_blocks = std::max(256 / wpb, f / (3 * wpb));
   }
-  // down: column slices of one wave-load, row groups to reach ~256 blocks of
-  // 16 waves (few blocks keep the number of y atomics low)
+  // down: column slices of one wave-load, row groups to reach at most
+  // kDownTargetBlocks blocks of 16 waves: two per CU (the kernel needs ~55
+  // VGPRs, so two 1024-thread blocks are resident at once).  Measured on the
+  // Qwen3-32B-shaped layer: ~256 blocks 19.6 us, ~384 18.2 us, ~512 16.7 us;
+  // the Qwen3-8B-shaped layer is unchanged (8.2 us).
   const int cw = 64 * (16 / static_cast<int>(elem_size(wdtype)));
   p.dn_col_slices = (d + cw - 1) / cw;
-  int rg = static_cast<int>(std::lround(256.0 / p.dn_col_slices));
+  int rg = std::max(1, kDownTargetBlocks / p.dn_col_slices);
   rg = std::max(1, std::min(f / 16, rg));
   // LDS per block: the 16 waves' partial rows plus (index, s) per row of the group
   const int red_bytes = (kDownThreads / 64) * cw * 4;

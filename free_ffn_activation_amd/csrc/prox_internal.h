@@ -17,6 +17,7 @@ constexpr int kStage1Unroll = 16;      // proxy rows loaded per lane per batch
 constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads)
 constexpr int kUgThreads = 256;        // up/gate kernel: threads per block
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
+constexpr int kDownTargetBlocks = 512;  // down kernel: at most this many blocks (two per CU)
 constexpr int kDownThreads = 1024;     // down kernel: 16 waves share one column slice
 constexpr int kFusedThreads = 1024;    // fused Stage-2 kernel: 16 waves per block, one block per CU
 constexpr int kFusedItems = 256;       // fused Stage-2 kernel: down items planned (the CU count of MI355X)
