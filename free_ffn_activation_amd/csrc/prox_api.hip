@@ -570,9 +570,14 @@ Plan make_plan(int d, int f, int wdtype) {
   rps = std::min(rps, 2048);  // bounds the LDS list of kept rows (20 B per row)
   p.rows_per_split = rps;
   p.splits = (d + rps - 1) / rps;
-  {  // up/gate: about one wave per 3 channels (at least 256 waves)
+  {  // up/gate: about one wave per 3 channels (at least 256 waves), in whole
+     // rounds of kUgResidentBlocks (the blocks resident at once: the kernel
+     // needs ~126 VGPRs, so four 4-wave blocks per CU): a partial last round
+     // pays the prologue again for a few blocks (Qwen3-32B-shaped layer: 2133
+     // blocks 32.1 us, 2048 31.7 us)
     const int wpb = kUgThreads / 64;
     p.ug_blocks = std::max(256 / wpb, f / (3 * wpb));
+    if (p.ug_blocks > kUgResidentBlocks) p.ug_blocks = p.ug_blocks / kUgResidentBlocks * kUgResidentBlocks;
   }
   // down: column slices of one wave-load, row groups to reach at most
   // kDownTargetBlocks blocks of 16 waves: two per CU (the kernel needs ~55

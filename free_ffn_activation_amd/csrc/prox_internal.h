@@ -15,6 +15,7 @@ namespace prox {
 constexpr int kThreads = 256;          // every kernel uses 4 waves of 64
 constexpr int kStage1Unroll = 16;      // proxy rows loaded per lane per batch
 constexpr int kUpGateUnroll = 8;       // 16-B steps per channel batch (x2 loads)
+constexpr int kUgResidentBlocks = 1024;  // up/gate: blocks resident at once (4 per CU over 256 CUs)
 constexpr int kUgThreads = 256;        // up/gate kernel: threads per block
 constexpr int kDownUnroll = 8;         // W_down rows per wave per batch
 constexpr int kDownTargetBlocks = 512;  // down kernel: at most this many blocks (two per CU)
