@@ -153,14 +153,15 @@ UpGateArgs upgate_args(const Plan& p, const prox_layer* L, const void* x, void* 
 }
 
 DownArgs down_args(const Plan& p, const prox_layer* L, void* ws, const int* mask_idx,
-                   const int* mask_count, float* y) {
+                   const int* mask_count, float* y, int tokens) {
   DownArgs a;
   a.d = p.d;
   a.f = p.f;
+  const DownGroups g = down_groups(p, tokens);
   a.col_slices = p.dn_col_slices;
-  a.row_groups = p.dn_row_groups;
-  a.max_rows = p.dn_max_rows;
-  a.chan_per_group = p.dn_chan_per_group;
+  a.row_groups = g.row_groups;
+  a.max_rows = g.max_rows;
+  a.chan_per_group = g.chan_per_group;
   a.w_down = L->w_down;
   a.ws = static_cast<const uint8_t*>(ws);
   a.tok_bytes = p.tok_bytes;
@@ -392,11 +393,11 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
     return hip_fail(e, "hipEventRecord");
   if ((stages & PROX_STAGE_DOWN) && fgrid == 0) {
     if (!any2) {
-      e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, true, s);
+      e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y, batch), layer->wdtype, batch, true, s);
     } else {
       e = for_each_group(batch, [&](int g0, int nt) {
         if (!grouped2(nt))
-          return launch_down(down_args(p, layer, ws_at(g0), mi_at(g0), mask_count + g0, y_at(g0)), layer->wdtype, nt,
+          return launch_down(down_args(p, layer, ws_at(g0), mi_at(g0), mask_count + g0, y_at(g0), nt), layer->wdtype, nt,
                              true, s);
         return launch_down_batch(down_batch_args(p, layer, ws_at(g0), nt), y_at(g0), s);
       });
@@ -546,6 +547,34 @@ prox_status proxy_state_all(const Plan& p, const prox_layer* layer, const void* 
 int proxy_row_stride(int f) { return ((f / 128) % 2 == 1) ? f : f + 128; }
 int proxy16_row_stride(int f) { return ((4 * f / 128) % 2 == 1) ? 4 * f : 4 * f + 128; }
 
+// Row groups of the down kernel for a launch over `tokens` tokens (the grid
+// is column slices x row groups x tokens).  One token: at most
+// kDownTargetBlocks blocks of 16 waves, two per CU (the kernel needs ~55
+// VGPRs, so two 1024-thread blocks are resident at once); measured on the
+// Qwen3-32B-shaped layer: ~256 blocks 19.6 us, ~384 18.2 us, ~512 16.7 us, the
+// Qwen3-8B-shaped layer unchanged (8.2 us).  Two or more tokens: half that per
+// token (two tokens then fill the same two blocks per CU; with the one-token
+// target they ran in two rounds, 36.8 against 34.9 us for Stage 2 of two 8B
+// tokens).
+DownGroups down_groups(const Plan& p, int tokens) {
+  const int f = p.f;
+  const int cw = 64 * (16 / static_cast<int>(elem_size(p.wdtype)));
+  const int target = tokens <= 1 ? kDownTargetBlocks : kDownTargetBlocks / 2;
+  int rg = std::max(1, target / p.dn_col_slices);
+  rg = std::max(1, std::min(f / 16, rg));
+  // LDS per block: the 16 waves' partial rows plus (index, s) per row of the group
+  const int red_bytes = (kDownThreads / 64) * cw * 4;
+  const int max_rows_cap = (61440 - red_bytes) / 8;
+  rg = std::max(rg, (f + max_rows_cap - 1) / max_rows_cap);
+  // decode mode: a row group is a channel range of at most one channel per thread
+  rg = std::max(rg, (f + kDownThreads - 1) / kDownThreads);
+  DownGroups g;
+  g.chan_per_group = ((f + rg - 1) / rg + 31) / 32 * 32;
+  g.row_groups = (f + g.chan_per_group - 1) / g.chan_per_group;
+  g.max_rows = std::max((f + g.row_groups - 1) / g.row_groups, g.chan_per_group);
+  return g;
+}
+
 Plan make_plan(int d, int f, int wdtype) {
   Plan p;
   p.d = d;
@@ -579,25 +608,15 @@ Plan make_plan(int d, int f, int wdtype) {
     p.ug_blocks = std::max(256 / wpb, f / (3 * wpb));
     if (p.ug_blocks > kUgResidentBlocks) p.ug_blocks = p.ug_blocks / kUgResidentBlocks * kUgResidentBlocks;
   }
-  // down: column slices of one wave-load, row groups to reach at most
-  // kDownTargetBlocks blocks of 16 waves: two per CU (the kernel needs ~55
-  // VGPRs, so two 1024-thread blocks are resident at once).  Measured on the
-  // Qwen3-32B-shaped layer: ~256 blocks 19.6 us, ~384 18.2 us, ~512 16.7 us;
-  // the Qwen3-8B-shaped layer is unchanged (8.2 us).
+  // down: column slices of one wave-load; row groups per launch (down_groups)
   const int cw = 64 * (16 / static_cast<int>(elem_size(wdtype)));
   p.dn_col_slices = (d + cw - 1) / cw;
-  int rg = std::max(1, kDownTargetBlocks / p.dn_col_slices);
-  rg = std::max(1, std::min(f / 16, rg));
-  // LDS per block: the 16 waves' partial rows plus (index, s) per row of the group
-  const int red_bytes = (kDownThreads / 64) * cw * 4;
-  const int max_rows_cap = (61440 - red_bytes) / 8;
-  rg = std::max(rg, (f + max_rows_cap - 1) / max_rows_cap);
-  // decode mode: a row group is a channel range of at most one channel per thread
-  rg = std::max(rg, (f + kDownThreads - 1) / kDownThreads);
-  p.dn_chan_per_group = ((f + rg - 1) / rg + 31) / 32 * 32;
-  rg = (f + p.dn_chan_per_group - 1) / p.dn_chan_per_group;
-  p.dn_row_groups = rg;
-  p.dn_max_rows = std::max((f + rg - 1) / rg, p.dn_chan_per_group);
+  {
+    const DownGroups g = down_groups(p, 1);
+    p.dn_row_groups = g.row_groups;
+    p.dn_chan_per_group = g.chan_per_group;
+    p.dn_max_rows = g.max_rows;
+  }
   // batched down: 512-column slices, about 256 blocks; a group holds at most
   // 2048 union ordinals (LDS)
   p.dnb_col_slices = (d + 511) / 512;
@@ -999,7 +1018,7 @@ PROX_API prox_status prox_ffn_stage2(const prox_layer* layer, const void* x, int
     hipError_t e = launch_upgate(upgate_args(p, layer, x, ws, mi, mc, y), layer->wdtype, batch,
                                  p.ug_blocks, false, s);
     if (e != hipSuccess) return hip_fail(e, "stage-2 up/gate launch");
-    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y), layer->wdtype, batch, false, s);
+    e = launch_down(down_args(p, layer, ws, mask_idx, mask_count, y, batch), layer->wdtype, batch, false, s);
     if (e != hipSuccess) return hip_fail(e, "stage-2 down launch");
     return PROX_OK;
   } catch (...) {

@@ -47,6 +47,8 @@ struct Plan {
   int dn_row_groups;
   int dn_max_rows;   // max rows per group (list mode) / LDS rows
   int dn_chan_per_group;  // decode mode: channels per row group (multiple of 32, <= 1024)
+  // (dn_row_groups, dn_max_rows and dn_chan_per_group are those of a
+  // one-token launch; down_groups gives them for any token count)
   // batched down (groups of 2..8 tokens): 512-column slices x groups of union ordinals
   int dnb_col_slices;
   int dnb_groups;
@@ -65,6 +67,12 @@ struct Plan {
 };
 
 Plan make_plan(int d, int f, int wdtype);
+
+// Down kernel row groups for a launch over `tokens` tokens
+struct DownGroups {
+  int row_groups, chan_per_group, max_rows;
+};
+DownGroups down_groups(const Plan& p, int tokens);
 
 struct Stage1Args {
   int d, f, splits, rows_per_split, n_panels, panel, proxy_stride;
