@@ -81,7 +81,7 @@ KERNELS = {
     "stage2_fused": (("stage2_fused.hip", "stage2_common.h"), ("stage2_fused_kernel<prox::Bf16Tag>",)),
     "stage2_upgate": (("stage2_upgate.hip", "stage2_common.h"), ("upgate_kernel<prox::Bf16Tag, true>",)),
     "stage2_down": (("stage2_down.hip", "stage2_common.h"), ("down_kernel<prox::Bf16Tag, true>",)),
-    "stage1_proxy_batch": (("stage1_batch.hip",), ("stage1_batch_kernel<prox::Bf16Tag, false>",)),
+    "stage1_proxy_batch": (("stage1_qt.hip", "stage1_mfma.h"), ("stage1_qt_kernel<prox::Bf16Tag, false, 1>",)),
     "stage2_upgate_batch": (("stage2_batch.hip",), ("upgate_batch_kernel",)),
     "stage2_down_batch": (("stage2_batch.hip",), ("down_batch_kernel", "down_reduce_kernel")),
 }
@@ -764,16 +764,22 @@ def batch_union_counts(rot, taus, B, o):
 def batch8_section(rot, taus, args):
     """Eight independent tokens per step through one layer (each token its
     own masks): the rotation's layers with their 16 tokens taken 8 at a time.
-    Timed three ways on the same schedule: the grouped kernels (union of the
-    tokens' rows and channels read once), the per-token kernels
-    (PROX_STAGE_PER_TOKEN: each token reads its own), torch's dense bf16 FFN
-    at M = 8.  Required bytes use the union counts: K_x^U * d_ff + 8 K_x^U +
-    3 K_s^U * d * 2 + 8 (2d + 4d) + 4 sum(k_s)."""
+    Timed three ways on the same schedule: the grouped kernels (Stage 1 from
+    the layers' channel-major proxy copies, every proxy row read once;
+    Stage 2 reads the union of the tokens' channels once), the per-token
+    kernels (PROX_STAGE_PER_TOKEN: each token reads its own rows and
+    channels), torch's dense bf16 FFN at M = 8.  Required bytes use the union
+    counts: K_x^U * d_ff + 8 K_x^U + 3 K_s^U * d * 2 + 8 (2d + 4d) +
+    4 sum(k_s) (eight tokens that each keep half of the rows leave K_x^U
+    within 1% of d)."""
     import numpy as np
     import torch
     from free_ffn_activation_amd import prox
     B = 8
     d, f, n_layers = rot.d, rot.f, rot.n_layers
+    for L in rot.layers:
+        L.add_proxy_qt()
+    torch.cuda.synchronize()
     K = max(1, args.steps)
     nb = rot.n_tok // B
     sched_b = [(s % n_layers, (s // n_layers) % nb) for s in range(n_layers * nb)]
@@ -1010,6 +1016,8 @@ def pmc_run(args) -> None:
         kernels = {nm: float(np.mean(by[nm])) for nm in STAGE_NAMES}
         launches = int(kx.size)
     else:
+        for L in rot.layers:
+            L.add_proxy_qt()
         _kxu, _ksu, _ks_sum, _kx_tok, by = batch_union_counts(rot, taus, B, Outs(rot.d, rot.f, B))
         kernels = {nm + "_batch": float(np.mean(by[nm])) for nm in STAGE_NAMES}
         launches = int(by["step"].size)

@@ -23,7 +23,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libprox.so")
 LIB_HOSTSAN = os.path.join(PKG, "libprox_hostsan.so")
-SOURCES = ["prox_api.hip", "stage1.hip", "stage1_batch.hip", "stage2_upgate.hip", "stage2_down.hip",
+SOURCES = ["prox_api.hip", "stage1.hip", "stage1_batch.hip", "stage1_qt.hip", "stage2_upgate.hip", "stage2_down.hip",
            "stage2_fused.hip", "stage2_batch.hip", "stage1_w16.hip", "pack.hip"]
 
 FLAGS = [

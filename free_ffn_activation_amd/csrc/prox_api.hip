@@ -74,6 +74,8 @@ prox_status check_layer(const prox_layer* L) {
     return fail(PROX_ERR_INVALID_ARG, "layer->proxy_kind %d is neither PROX_PROXY_INT4 nor PROX_PROXY_W16",
                 L->proxy_kind);
   }
+  if (L->proxy_qt && (L->proxy_kind != PROX_PROXY_INT4 || !aligned(L->proxy_qt, 16)))
+    return fail(PROX_ERR_INVALID_ARG, "layer proxy_qt must be 16-byte aligned and belongs to PROX_PROXY_INT4 layers");
   if (!L->w_upgate_t || !L->w_down) return fail(PROX_ERR_INVALID_ARG, "layer buffer pointer is NULL");
   if (!aligned(L->w_upgate_t, 16) || !aligned(L->w_down, 16))
     return fail(PROX_ERR_INVALID_ARG, "layer buffers must be 16-byte aligned");
@@ -219,6 +221,37 @@ hipError_t for_each_group(int32_t batch, Fn fn) {
   return hipSuccess;
 }
 
+// CUs of the current device (the channel-major Stage-1 grid: one block per
+// CU), cached per device; 256 if the query fails.
+int device_cus();
+
+// Channel-major Stage 1 of one group of nt tokens (ws: the group's first slice).
+QtArgs qt_args(const Plan& p, const prox_layer* L, const void* x, float tau_x, float tau_s, void* ws,
+               float* s_tilde, int* in_count, int nt) {
+  QtArgs a = qt_plan(p.d, p.f, device_cus());
+  a.nt = nt;
+  a.act = L->activation;
+  a.proxy_qt = static_cast<const uint8_t*>(L->proxy_qt);
+  a.proxy_scale = L->proxy_scale;
+  a.x = x;
+  a.tau_x = tau_x;
+  a.tau_s = tau_s;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.tok_bytes = p.tok_bytes;
+  a.off_bitmap = p.off_bitmap;
+  a.s_tilde = s_tilde;
+  a.in_count = in_count;
+  return a;
+}
+
+// The channel-major Stage 1 for a group of nt tokens: when the layer has the
+// copy and the group's x and scales fit the device's LDS.
+bool qt_usable(const Plan& p, const prox_layer* L, int nt) {
+  QtArgs a = qt_plan(p.d, p.f, device_cus());
+  a.nt = nt;
+  return qt_fits(a, L->wdtype);
+}
+
 FusedArgs fused_args(const Plan& p, const prox_layer* L, const void* x, void* ws, int* mask_idx, int* mask_count,
                      float* y, uint32_t wait_ticks) {
   FusedArgs a;
@@ -281,6 +314,17 @@ int fused_grid(int wdtype, size_t smem) {
   return di.cus;
 }
 
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (g_dev.size() <= static_cast<size_t>(dev)) g_dev.resize(static_cast<size_t>(dev) + 1);
+  DevInfo& di = g_dev[static_cast<size_t>(dev)];
+  if (di.cus == 0 && hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    di.cus = 0;
+  return di.cus > 0 ? di.cus : 256;
+}
+
 // Checks of prox_ffn_decode's arguments other than the workspace.
 prox_status check_decode_args(const prox_layer* layer, const void* x, int32_t batch, float tau_x, float tau_s,
                               const float* y, const int32_t* mask_idx, const int32_t* mask_count,
@@ -324,10 +368,18 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
     return (stages & PROX_STAGE_GROUPED) != 0 || nt >= kGroupedMinTokens;
   };
   auto grouped2 = [&](int nt) { return grouped1(nt) && layer->wdtype == PROX_BF16; };
+  // Stage 1 from the channel-major proxy copy, when the layer has one: for
+  // the groups that take the grouped kernels (faster than the union-of-rows
+  // Stage 1 there; for two tokens the per-token Stage 1 is faster still)
+  auto qt1 = [&](int nt) {
+    return layer->proxy_qt != nullptr && layer->proxy_kind == PROX_PROXY_INT4 && nt >= 2 &&
+           !(stages & PROX_STAGE_PER_TOKEN) &&
+           ((stages & PROX_STAGE_GROUPED) != 0 || nt >= kGroupedMinTokens) && qt_usable(p, layer, nt);
+  };
   bool any1 = false, any2 = false;
   for (int g0 = 0; g0 < batch; g0 += kBatchMax) {
     const int nt = std::min<int>(kBatchMax, batch - g0);
-    any1 = any1 || grouped1(nt);
+    any1 = any1 || grouped1(nt) || qt1(nt);
     any2 = any2 || grouped2(nt);
   }
   const size_t es = elem_size(layer->wdtype);
@@ -346,6 +398,9 @@ prox_status decode_impl(const prox_layer* layer, const void* x, int32_t batch, f
                         false, s);
     } else {
       e = for_each_group(batch, [&](int g0, int nt) {
+        if (qt1(nt))
+          return launch_stage1_qt(qt_args(p, layer, x_at(g0), tau_x, tau_s, ws_at(g0), nullptr, ic_at(g0), nt),
+                                  layer->wdtype, false, s);
         Stage1Args a1 = stage1_args(p, layer, x_at(g0), tau_x, tau_s, ws_at(g0), nullptr, ic_at(g0));
         if (!grouped1(nt)) return launch_stage1(a1, layer->wdtype, nt, false, s);
         a1.nt = nt;
@@ -840,6 +895,37 @@ PROX_API prox_status prox_workspace_init(void* ws, size_t ws_bytes, void* stream
   }
 }
 
+PROX_API prox_status prox_proxy_qt_size(int32_t d, int32_t f, size_t* bytes) {
+  try {
+    g_err.clear();
+    if (!bytes) return fail(PROX_ERR_INVALID_ARG, "bytes is NULL");
+    prox_status st = check_shape(d, f, PROX_BF16);
+    if (st != PROX_OK) return st;
+    *bytes = proxy_qt_bytes(d, f);
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+PROX_API prox_status prox_pack_proxy_qt(const prox_layer* layer, void* stream) {
+  try {
+    g_err.clear();
+    prox_status st = check_layer(layer);
+    if (st != PROX_OK) return st;
+    if (layer->proxy_kind != PROX_PROXY_INT4)
+      return fail(PROX_ERR_UNSUPPORTED, "the channel-major copy is of the INT4 proxy (PROX_PROXY_INT4 layers)");
+    if (!layer->proxy_qt) return fail(PROX_ERR_INVALID_ARG, "layer->proxy_qt is NULL");
+    const hipError_t e = launch_pack_qt(static_cast<const uint8_t*>(layer->proxy_q), proxy_row_stride(layer->d_ff),
+                                        layer->d_model, layer->d_ff, static_cast<uint8_t*>(layer->proxy_qt),
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pack_qt launch");
+    return PROX_OK;
+  } catch (...) {
+    return fail(PROX_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
 PROX_API prox_status prox_proxy16_size(int32_t d, int32_t f, int32_t wdtype, size_t* bytes) {
   try {
     g_err.clear();
@@ -1048,6 +1134,9 @@ PROX_API prox_status prox_proxy_state(const prox_layer* layer, const void* x, in
         Stage1Args a1 = stage1_args(p, layer, static_cast<const uint8_t*>(x) + static_cast<size_t>(g0) * p.d * es,
                                     tau_x, INFINITY, static_cast<uint8_t*>(ws) + static_cast<size_t>(g0) * p.tok_bytes,
                                     s_tilde + static_cast<size_t>(g0) * p.f, in_count ? in_count + g0 : nullptr);
+        if (layer->proxy_qt != nullptr && nt >= kGroupedMinTokens && qt_usable(p, layer, nt))
+          return launch_stage1_qt(qt_args(p, layer, a1.x, tau_x, INFINITY, a1.ws, a1.s_tilde, a1.in_count, nt),
+                                  layer->wdtype, true, s);
         if (nt < kGroupedMinTokens) return launch_stage1(a1, layer->wdtype, nt, true, s);
         a1.nt = nt;
         return launch_stage1_batch(a1, layer->wdtype, true, s);

@@ -91,6 +91,32 @@ struct Stage1Args {
   const void* proxy_w16;  // PROX_PROXY_W16: [d][proxy16_stride] bf16 rows
 };
 
+// Stage 1 of a group of nt <= kBatchMax tokens from the channel-major copy of
+// the INT4 proxy (proxy_qt).  Grid: nb blocks, block b owning 16-channel
+// groups [b ng / nb, (b + 1) ng / nb); each group's K range is cut into
+// `parts` contiguous ranges of ncp 128-row chunks (the last may run past d).
+struct QtArgs {
+  int d, f, nt, act;
+  int nck;        // 128-row chunks of the K range, ceil(d / 128)
+  int parts;      // 1, 2 or 4
+  int ncp;        // chunks per part, ceil(nck / parts)
+  int ng, nb;     // 16-channel groups (f / 16) and blocks
+  int s_waves;    // streaming waves per block (all 16 build operands, the rest only that)
+  int upw;        // units (group, part) per streaming wave: 1 or 2
+  const uint8_t* proxy_qt;
+  const float* proxy_scale;
+  const void* x;  // [nt][d]
+  float tau_x, tau_s;
+  uint8_t* ws;    // the group's first token slice
+  size_t tok_bytes, off_bitmap;
+  float* s_tilde; // [nt][f] or nullptr
+  int* in_count;  // [nt] or nullptr
+};
+
+// Plan of the channel-major Stage-1 kernel for (d, f); `blocks` is the grid cap.
+QtArgs qt_plan(int d, int f, int blocks);
+size_t proxy_qt_bytes(int d, int f);
+
 // Batched Stage 2 (bf16 weights), one group of nt <= kBatchMax tokens; ws is
 // the group's first token slice, token t's slice is ws + t * tok_bytes.
 struct UpGateBatchArgs {
@@ -153,6 +179,12 @@ hipError_t launch_stage2_fused(const FusedArgs& a, int wdtype, int grid, hipStre
 hipError_t fused_occupancy(int wdtype, size_t smem, int* blocks_per_cu);
 size_t fused_smem(const FusedArgs& a);
 hipError_t launch_stage1_batch(const Stage1Args& a, int wdtype, bool write_state, hipStream_t s);
+hipError_t launch_stage1_qt(const QtArgs& a, int wdtype, bool write_state, hipStream_t s);
+// whether the channel-major Stage 1 of this plan fits the kernel's waves and
+// the device's LDS (x of the group's tokens and the scales are staged there);
+// if not, the union-of-rows Stage 1 runs instead
+bool qt_fits(const QtArgs& a, int wdtype);
+hipError_t launch_pack_qt(const uint8_t* proxy_q, int qstride, int d, int f, uint8_t* proxy_qt, hipStream_t s);
 hipError_t launch_stage1_w16(const Stage1Args& a, int batch, bool write_state, hipStream_t s);
 int proxy16_row_stride(int f);
 hipError_t launch_pack16(const void* w_up, const void* w_gate, int d, int f, int stride, void* proxy_w16,

@@ -42,6 +42,7 @@ _STATUS_NAMES = {0: "PROX_OK", -1: "PROX_ERR_INVALID_ARG", -2: "PROX_ERR_UNSUPPO
 EXPORTED = ("prox_abi_version", "prox_last_error", "prox_layer_sizes", "prox_workspace_size",
             "prox_calibrate_workspace_size", "prox_budget_effective", "prox_budget_s2",
             "prox_workspace_init", "prox_pack_proxy", "prox_proxy16_size", "prox_pack_proxy16",
+            "prox_proxy_qt_size", "prox_pack_proxy_qt",
             "prox_calibrate", "prox_calibrate_hist_workspace_size", "prox_calibrate_hist", "prox_ffn_decode", "prox_ffn_decode_noalloc", "prox_ffn_decode_events",
             "prox_ffn_decode_stages", "prox_ffn_stage2", "prox_proxy_state", "prox_workspace_check",
             "prox_set_wait_limit")
@@ -64,7 +65,8 @@ _c_i32, _c_f32, _c_size, _c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 class prox_layer(ctypes.Structure):
     _fields_ = [("d_model", _c_i32), ("d_ff", _c_i32), ("wdtype", _c_i32), ("activation", _c_i32),
                 ("proxy_q", _c_vp), ("proxy_scale", _c_vp), ("w_upgate_t", _c_vp),
-                ("w_down", _c_vp), ("proxy_kind", _c_i32), ("reserved", _c_i32), ("proxy_w16", _c_vp)]
+                ("w_down", _c_vp), ("proxy_kind", _c_i32), ("reserved", _c_i32), ("proxy_w16", _c_vp),
+                ("proxy_qt", _c_vp)]
 
 
 _P = ctypes.POINTER
@@ -83,6 +85,8 @@ _sig = {
     "prox_pack_proxy": (_c_i32, [_c_vp, _c_vp, _c_vp, _P(prox_layer), _c_vp]),
     "prox_proxy16_size": (_c_i32, [_c_i32, _c_i32, _c_i32, _P(_c_size)]),
     "prox_pack_proxy16": (_c_i32, [_c_vp, _c_vp, _P(prox_layer), _c_vp]),
+    "prox_proxy_qt_size": (_c_i32, [_c_i32, _c_i32, _P(_c_size)]),
+    "prox_pack_proxy_qt": (_c_i32, [_P(prox_layer), _c_vp]),
     "prox_calibrate": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _P(_c_f32),
                                 _P(_c_f32), _c_vp, _c_size, _c_vp]),
     "prox_ffn_decode": (_c_i32, [_P(prox_layer), _c_vp, _c_i32, _c_f32, _c_f32, _c_vp, _c_vp,
@@ -200,12 +204,35 @@ class ProxLayer:
         self.w_down = torch.empty(sizes[3] // es, dtype=wt, device=device)
         self.proxy_w16 = (torch.zeros(prox_proxy16_size(d_model, d_ff, wdtype), dtype=torch.uint8, device=device)
                           if proxy16 else None)
+        self.proxy_qt = None
+        self.use_qt = True
         self.desc = self._make_desc()
 
     def _make_desc(self) -> prox_layer:
+        qt = (self.proxy_qt.data_ptr()
+              if (self.proxy_qt is not None and self.use_qt and self.proxy_kind == PROX_PROXY_INT4) else None)
         return prox_layer(self.d_model, self.d_ff, self.wdtype, self.activation, self.proxy_q.data_ptr(),
                           self.proxy_scale.data_ptr(), self.w_upgate_t.data_ptr(), self.w_down.data_ptr(),
-                          self.proxy_kind, 0, self.proxy_w16.data_ptr() if self.proxy_w16 is not None else None)
+                          self.proxy_kind, 0, self.proxy_w16.data_ptr() if self.proxy_w16 is not None else None,
+                          qt)
+
+    def add_proxy_qt(self, stream=None, device="cuda") -> None:
+        """Allocate the channel-major proxy copy (proxy_qt) and fill it from the
+        packed proxy_q (call after prox_pack_proxy)."""
+        if self.proxy_qt is None:
+            self.proxy_qt = torch.empty(prox_proxy_qt_size(self.d_model, self.d_ff), dtype=torch.uint8,
+                                        device=device)
+            self.desc = self._make_desc()
+        prox_pack_proxy_qt(self, stream)
+
+    def with_qt(self, use: bool) -> "ProxLayer":
+        """Another descriptor over the same buffers with proxy_qt passed (True)
+        or left out (False, so groups take the union-of-rows Stage 1)."""
+        other = object.__new__(ProxLayer)
+        other.__dict__.update(self.__dict__)
+        other.use_qt = use
+        other.desc = other._make_desc()
+        return other
 
     def with_activation(self, activation: int) -> "ProxLayer":
         """Another descriptor over the same packed buffers with a different gate
@@ -240,6 +267,8 @@ class ProxLayer:
         bufs = [self.proxy_q, self.proxy_scale, self.w_upgate_t, self.w_down]
         if self.proxy_w16 is not None:
             bufs.append(self.proxy_w16)
+        if self.proxy_qt is not None:
+            bufs.append(self.proxy_qt)
         return sum(t.numel() * t.element_size() for t in bufs)
 
 
@@ -278,6 +307,19 @@ def prox_pack_proxy16(W_up: torch.Tensor, W_gate: torch.Tensor, layer: ProxLayer
     if layer.proxy_w16 is None:
         raise ValueError("layer has no 16-bit proxy buffer (ProxLayer(..., proxy16=True))")
     _check(_lib.prox_pack_proxy16(_ptr(W_up), _ptr(W_gate), ctypes.byref(layer.desc), _stream(stream)))
+
+
+def prox_proxy_qt_size(d_model: int, d_ff: int) -> int:
+    out = _c_size()
+    _check(_lib.prox_proxy_qt_size(d_model, d_ff, ctypes.byref(out)))
+    return int(out.value)
+
+
+def prox_pack_proxy_qt(layer: ProxLayer, stream=None) -> None:
+    if layer.proxy_qt is None:
+        raise ValueError("layer has no proxy_qt buffer (ProxLayer.add_proxy_qt)")
+    desc = layer.desc if layer.use_qt else layer.with_qt(True).desc
+    _check(_lib.prox_pack_proxy_qt(ctypes.byref(desc), _stream(stream)))
 
 
 def prox_calibrate(layer: ProxLayer, X_cal: torch.Tensor, keep_x: float, sparsity_s: float,

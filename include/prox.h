@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PROX_ABI_VERSION 3
+#define PROX_ABI_VERSION 4
 
 typedef enum {
   PROX_OK = 0,
@@ -101,6 +101,29 @@ typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
  *             column groups of proxy_q: each group of 16 output columns takes
  *             64 bytes, the 16 up values then the 16 gate values.
  * With PROX_PROXY_W16, proxy_q and proxy_scale may be NULL.
+ * proxy_qt    optional (NULL = absent): a channel-major copy of proxy_q for
+ *             groups of tokens (prox_pack_proxy_qt; PROX_PROXY_INT4 only).
+ *             When present, Stage 1 of every group that runs the grouped
+ *             kernels (3..8 tokens, or 2 when they are forced) of a decode,
+ *             and of every group of 3..8 tokens of prox_proxy_state, reads it
+ *             instead of the union of the tokens' proxy rows: every proxy row
+ *             once, as contiguous 1 KB runs, with no partial sums between
+ *             blocks.  A group whose x (d_model values per token) and proxy
+ *             scales (8 bytes per input row) do not fit in one CU's LDS
+ *             beside the kernel's operand buffers (16 to 64 KB) runs the
+ *             union-of-rows Stage 1 instead.
+ *             Results are those of the method either way; the two Stage-1
+ *             kernels round the proxy state differently (well within the
+ *             decode's documented tolerance).  Layout, for 16-channel group g
+ *             (channels 16g .. 16g+15, g < d_ff / 16) and 128-row chunk k of
+ *             the inputs (rows 128k .. 128k+127; rows past d_model hold code
+ *             0): 2048 bytes at offset (k * (d_ff / 16) + g) * 2048 (chunk-
+ *             major), the up codes then the gate codes, 1024 bytes each.  In each 1024-byte
+ *             half, the 16 bytes at 16 * l (l = 0..63) hold channel 16g + l % 16
+ *             and rows 128k + 32 (l / 16) + 8s + e for s = 0..3 (the 4-byte
+ *             word s) and e = 0..7, row e of word s in nibble
+ *             {0, 4, 1, 5, 2, 6, 3, 7}[e] (nibble 0 = bits 0..3), each nibble
+ *             code + 8 as in proxy_q.  Bytes: prox_proxy_qt_size().
  */
 typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
 typedef enum { PROX_PROXY_INT4 = 0, PROX_PROXY_W16 = 1 } prox_proxy_kind;
@@ -117,6 +140,7 @@ typedef struct {
   int32_t proxy_kind; /* prox_proxy_kind */
   int32_t reserved;
   void* proxy_w16;
+  void* proxy_qt;
 } prox_layer;
 
 /* Version of this ABI (PROX_ABI_VERSION). */
@@ -178,6 +202,23 @@ prox_status prox_workspace_init(void* ws, size_t ws_bytes, void* stream);
  */
 prox_status prox_pack_proxy(const void* W_up, const void* W_gate, const void* W_down,
                             const prox_layer* out, void* stream);
+
+/*
+ * Bytes of the channel-major proxy copy (proxy_qt, layout at prox_layer):
+ * d_ff * 128 * ceil(d_model / 128), i.e. d_model * d_ff when d_model is a
+ * multiple of 128.
+ */
+prox_status prox_proxy_qt_size(int32_t d_model, int32_t d_ff, size_t* bytes);
+
+/*
+ * Fills layer->proxy_qt (device, 16-byte aligned, prox_proxy_qt_size bytes)
+ * from layer->proxy_q, which must already hold the packed proxy on `stream`
+ * (prox_pack_proxy): a pure re-layout of the same codes, no arithmetic on
+ * weights ([blog] "Stage 1": the INT4 proxy, here stored a second way for
+ * groups of tokens).  PROX_PROXY_INT4 layers only (PROX_ERR_UNSUPPORTED
+ * otherwise).  Asynchronous.
+ */
+prox_status prox_pack_proxy_qt(const prox_layer* layer, void* stream);
 
 /*
  * Bytes of the 16-bit proxy (proxy_w16) of a bf16 layer: d_model * wstride.
@@ -255,7 +296,8 @@ prox_status prox_calibrate_hist(const prox_layer* layer, const void* X_cal, int3
  * (prox_ffn_decode_stages can force either).  Grouped (the pages study
  * batch 1 and leave larger batches open, [blog] limitations section): Stage 1
  * reads each proxy row of the union of the group's kept input rows once and
- * gives a token a zero weight on the rows it rejects; for bf16 weights Stage 2
+ * gives a token a zero weight on the rows it rejects (with layer->proxy_qt:
+ * every proxy row, from the channel-major copy); for bf16 weights Stage 2
  * reads each channel of the union of the group's channel lists once (s = 0
  * for a token that drops the channel) and adds the down projection's partial
  * sums in fixed order, so y is reproducible bit for bit; fp32 layers run

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_sizes():
-    assert P.prox_abi_version() == 3
+    assert P.prox_abi_version() == 4
     s = P.prox_layer_sizes(4096, 12288, P.PROX_BF16)
     assert s == (4096 * (12288 + 128), 2 * 4096 * 4, 2 * 12288 * 4096 * 2, 12288 * 4096 * 2)
     assert P.prox_layer_sizes(128, 384, P.PROX_BF16)[0] == 128 * 384     # 384/128 odd: no padding
@@ -63,7 +63,7 @@ FAKE = 1 << 40  # a 256-aligned address that is never dereferenced by validation
 
 
 def _layer(d=256, f=768, dt=0, **kw):
-    L = P.prox_layer(d, f, dt, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, None)
+    L = P.prox_layer(d, f, dt, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, None, None)
     for k, v in kw.items():
         setattr(L, k, v)
     return L
@@ -88,6 +88,10 @@ def test_decode_argument_validation():
     assert _decode(_layer(dt=P.PROX_BF16, proxy_kind=P.PROX_PROXY_W16)) == P.PROX_ERR_INVALID_ARG
     assert _decode(_layer(proxy_kind=P.PROX_PROXY_W16, proxy_w16=FAKE)) == P.PROX_ERR_UNSUPPORTED
     assert _decode(_layer(dt=P.PROX_BF16, proxy_kind=P.PROX_PROXY_W16, proxy_w16=FAKE + 8)) == P.PROX_ERR_INVALID_ARG
+    # the channel-major proxy copy: aligned, and only beside the INT4 proxy
+    assert _decode(_layer(proxy_qt=FAKE + 8)) == P.PROX_ERR_INVALID_ARG
+    assert _decode(_layer(dt=P.PROX_BF16, proxy_kind=P.PROX_PROXY_W16, proxy_w16=FAKE,
+                          proxy_qt=FAKE)) == P.PROX_ERR_INVALID_ARG
     assert _decode(_layer(d=250)) == P.PROX_ERR_UNSUPPORTED
     assert _decode(_layer(w_down=FAKE + 8)) == P.PROX_ERR_INVALID_ARG     # misaligned
     assert _decode(ok_layer, batch=0) == P.PROX_ERR_INVALID_ARG
@@ -181,3 +185,20 @@ def test_noalloc_rejects_before_touching_a_device():
     st = lib.prox_ffn_decode_noalloc(None, FAKE, 1, 0.5, 0.1, FAKE, FAKE, FAKE, None, None)
     assert st == P.PROX_ERR_INVALID_ARG
     assert P.PROX_NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+def test_proxy_qt_size_and_pack_validation():
+    # d_ff * 128 * ceil(d_model / 128): whole 128-row chunks of every channel
+    assert P.prox_proxy_qt_size(4096, 12288) == 4096 * 12288
+    assert P.prox_proxy_qt_size(5120, 25600) == 5120 * 25600
+    assert P.prox_proxy_qt_size(320, 384) == 384 * 128 * 3
+    with pytest.raises(P.ProxError) as ei:
+        P.prox_proxy_qt_size(100, 384)
+    assert ei.value.status == P.PROX_ERR_UNSUPPORTED
+    lib = P.raw_library()
+    assert lib.prox_proxy_qt_size(256, 768, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_pack_proxy_qt(None, None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_pack_proxy_qt(ctypes.byref(_layer()), None) == P.PROX_ERR_INVALID_ARG   # no proxy_qt
+    assert lib.prox_pack_proxy_qt(ctypes.byref(_layer(proxy_qt=FAKE + 4)), None) == P.PROX_ERR_INVALID_ARG
+    assert lib.prox_pack_proxy_qt(ctypes.byref(_layer(dt=P.PROX_BF16, proxy_kind=P.PROX_PROXY_W16,
+                                                      proxy_w16=FAKE)), None) == P.PROX_ERR_UNSUPPORTED
