@@ -66,26 +66,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 // union ordinals [u0, u0 + kSlice) of this block go to s_ch (channel) and s_tb
 // (bit t set when token t keeps the channel) and to ulist; each token's index
 // list receives the entries of those channels; block 0 publishes U (at
-// ulist[f]) and every token's k_s.  Returns U.  The bitmap is read in passes
-// of one word per thread per token; a block scan of the 1 + nt popcounts
-// gives every word its union and per-token prefixes.  The slice is then
-// filled with all lanes of a wave on the 32 bits of one overlapping word at a
-// time (its data broadcast with readlane), not by the word's own thread.
-// The first pass's words come preloaded (union_words), so that a caller can
-// issue other loads behind them before the block's first barrier.
+// ulist[f]) and every token's k_s.  Returns U.  Every thread reads
+// kUnionWords consecutive words of each token's bitmap per round (one round
+// up to d_ff = 32768 for 256 threads, so one round trip); a block scan of the
+// 1 + nt popcounts of each thread gives its words their union and per-token
+// prefixes.  The slice is then filled with all lanes of a wave on the 32 bits
+// of one overlapping word at a time (its data broadcast with readlane), not
+// by the word's own thread.  The first round's words come preloaded
+// (union_words), so that a caller can issue other loads behind them before
+// the block's first barrier.
+constexpr int kUnionWords = 4;
 template <int kNT>
-__device__ __forceinline__ void union_words(const UpGateBatchArgs& a, int pass, uint32_t (&tw)[kBatchMax]) {
-  const int nw = a.f / 32;
-  const int w = min(pass * kNT + static_cast<int>(threadIdx.x), nw - 1);
+__device__ __forceinline__ void union_words(const UpGateBatchArgs& a, int round, u32x4_t (&tw)[kBatchMax]) {
+  const int nw = a.f / 32;  // a multiple of 4 (d_ff % 128 == 0)
+  const int w0 = (round * kNT + static_cast<int>(threadIdx.x)) * kUnionWords;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int t = 0; t < kBatchMax; ++t)
-    tw[t] = reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(min(t, a.nt - 1)) * a.tok_bytes +
-                                              a.off_bitmap)[w];
+  for (int t = 0; t < kBatchMax; ++t) {
+    const uint32_t* bm =
+        reinterpret_cast<const uint32_t*>(a.ws + static_cast<size_t>(min(t, a.nt - 1)) * a.tok_bytes + a.off_bitmap);
+    tw[t] = w0 < nw ? *reinterpret_cast<const u32x4_t*>(bm + w0) : z;
+  }
 }
 
 template <int kNT, int kSlice>
 __device__ __forceinline__ int union_slice(const UpGateBatchArgs& a, int u0, int (&s_scan)[2][kNT / 64][1 + kBatchMax],
-                                           int* s_ch, uint32_t* s_tb, uint32_t (&tw)[kBatchMax]) {
+                                           int* s_ch, uint32_t* s_tb, u32x4_t (&tw)[kBatchMax]) {
   constexpr int kW = kNT / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -93,38 +99,45 @@ __device__ __forceinline__ int union_slice(const UpGateBatchArgs& a, int u0, int
   const int f = a.f;
   const int nt = a.nt;
   const int nw = f / 32;
-  const int npass = (nw + kNT - 1) / kNT;
+  const int nrounds = (nw + kNT * kUnionWords - 1) / (kNT * kUnionWords);
   int* ulist = reinterpret_cast<int*>(a.ws + a.off_ulist);
   int base[1 + kBatchMax];
 #pragma unroll
   for (int q = 0; q <= kBatchMax; ++q) base[q] = 0;
-  for (int pass = 0; pass < npass; ++pass) {
-    const int w = pass * kNT + tid;
-    if (pass > 0) union_words<kNT>(a, pass, tw);
-    uint32_t uw = 0u;
+  for (int r = 0; r < nrounds; ++r) {
+    if (r > 0) union_words<kNT>(a, r, tw);
+    uint32_t uw[kUnionWords];
     int cnt[1 + kBatchMax];
 #pragma unroll
+    for (int q = 0; q <= kBatchMax; ++q) cnt[q] = 0;
+#pragma unroll
     for (int t = 0; t < kBatchMax; ++t) {
-      tw[t] = (t < nt && w < nw) ? tw[t] : 0u;
-      uw |= tw[t];
-      cnt[1 + t] = __popc(tw[t]);
+      if (t >= nt) tw[t] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < kUnionWords; ++i) cnt[1 + t] += __popc(tw[t][i]);
     }
-    cnt[0] = __popc(uw);
+#pragma unroll
+    for (int i = 0; i < kUnionWords; ++i) {
+      uw[i] = 0u;
+#pragma unroll
+      for (int t = 0; t < kBatchMax; ++t) uw[i] |= tw[t][i];
+      cnt[0] += __popc(uw[i]);
+    }
     int inc[1 + kBatchMax];
 #pragma unroll
     for (int q = 0; q <= kBatchMax; ++q) inc[q] = wave_inclusive_scan_int(cnt[q]);
     if (lane == 63) {
 #pragma unroll
-      for (int q = 0; q <= kBatchMax; ++q) s_scan[pass & 1][wave][q] = inc[q];
+      for (int q = 0; q <= kBatchMax; ++q) s_scan[r & 1][wave][q] = inc[q];
     }
     __syncthreads();
-    int excl[1 + kBatchMax];
+    int excl[1 + kBatchMax];  // prefixes at this thread's first word
 #pragma unroll
     for (int q = 0; q <= kBatchMax; ++q) {
       int pre = 0, tot = 0;
 #pragma unroll
       for (int v = 0; v < kW; ++v) {
-        const int c = s_scan[pass & 1][v][q];
+        const int c = s_scan[r & 1][v][q];
         pre += v < wave ? c : 0;
         tot += c;
       }
@@ -132,36 +145,44 @@ __device__ __forceinline__ int union_slice(const UpGateBatchArgs& a, int u0, int
       base[q] += tot;
     }
     // words of this wave that hold ordinals of the slice, one at a time
-    uint64_t ovm = __ballot(cnt[0] > 0 && excl[0] < u0 + kSlice && excl[0] + cnt[0] > u0);
-    while (ovm) {  // wave-uniform
-      const int src = static_cast<int>(__builtin_ctzll(ovm));
-      ovm &= ovm - 1ull;
-      const uint32_t su = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(uw), src));
-      const int se = __builtin_amdgcn_readlane(excl[0], src);
-      uint32_t st[kBatchMax];
-      int sx[kBatchMax];
 #pragma unroll
-      for (int t = 0; t < kBatchMax; ++t) {
-        st[t] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw[t]), src));
-        sx[t] = __builtin_amdgcn_readlane(excl[1 + t], src);
-      }
-      const int bit = lane & 31;
-      const uint32_t below = (1u << bit) - 1u;
-      const int o = se + __popc(su & below);
-      if (lane < 32 && ((su >> bit) & 1u) && o >= u0 && o < u0 + kSlice) {
-        const int j = (pass * kNT + wave * 64 + src) * 32 + bit;
-        uint32_t tb = 0u;
+    for (int i = 0; i < kUnionWords; ++i) {
+      const int cu = __popc(uw[i]);
+      uint64_t ovm = __ballot(cu > 0 && excl[0] < u0 + kSlice && excl[0] + cu > u0);
+      while (ovm) {  // wave-uniform
+        const int src = static_cast<int>(__builtin_ctzll(ovm));
+        ovm &= ovm - 1ull;
+        const uint32_t su = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(uw[i]), src));
+        const int se = __builtin_amdgcn_readlane(excl[0], src);
+        uint32_t st[kBatchMax];
+        int sx[kBatchMax];
 #pragma unroll
         for (int t = 0; t < kBatchMax; ++t) {
-          if ((st[t] >> bit) & 1u) {
-            tb |= 1u << t;
-            a.mask_idx[static_cast<size_t>(t) * f + sx[t] + __popc(st[t] & below)] = j;
-          }
+          st[t] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw[t][i]), src));
+          sx[t] = __builtin_amdgcn_readlane(excl[1 + t], src);
         }
-        s_ch[o - u0] = j;
-        s_tb[o - u0] = tb;
-        ulist[o] = j;
+        const int bit = lane & 31;
+        const uint32_t below = (1u << bit) - 1u;
+        const int o = se + __popc(su & below);
+        if (lane < 32 && ((su >> bit) & 1u) && o >= u0 && o < u0 + kSlice) {
+          const int j = ((r * kNT + wave * 64 + src) * kUnionWords + i) * 32 + bit;
+          uint32_t tb = 0u;
+#pragma unroll
+          for (int t = 0; t < kBatchMax; ++t) {
+            if ((st[t] >> bit) & 1u) {
+              tb |= 1u << t;
+              a.mask_idx[static_cast<size_t>(t) * f + sx[t] + __popc(st[t] & below)] = j;
+            }
+          }
+          s_ch[o - u0] = j;
+          s_tb[o - u0] = tb;
+          ulist[o] = j;
+        }
       }
+      // prefixes at the next word
+      excl[0] += cu;
+#pragma unroll
+      for (int t = 0; t < kBatchMax; ++t) excl[1 + t] += __popc(tw[t][i]);
     }
   }
   if (blockIdx.x == 0 && tid == 0) {
@@ -186,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
   const int nt = a.nt;
 
   const int u0 = static_cast<int>(blockIdx.x) * kUgbChannels;
-  uint32_t tw[kBatchMax];
+  u32x4_t tw[kBatchMax];
   union_words<kThreads>(a, 0, tw);
   const int U = union_slice<kThreads, kUgbChannels>(a, u0, s_scan, s_ch, s_tb, tw);
   if (u0 >= U) return;  // block-uniform
