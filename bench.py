@@ -237,11 +237,20 @@ class Outs:
         self.ws = prox.new_workspace(d, f, b)
 
 
+# Device cycles of the spin kernel queued ahead of a timed region (about
+# 0.4 ms): the start event then executes after the host has queued the
+# replays, so the host's submission latency of the first graph (tens of us)
+# is not counted as GPU time of the K steps.
+LEAD_CYCLES = 1_000_000
+
+
 def time_graph(fn, steps_per_round: int, K: int, label: str, graph: bool = True) -> float:
     """Exactly K steps (fn(0) .. fn(K-1)) replayed from HIP graphs (whole
     rotations of steps_per_round steps, then a graph of the first
-    K mod steps_per_round), bracketed by HIP events on the current stream.
-    Returns microseconds per step."""
+    K mod steps_per_round), bracketed by HIP events on the current stream,
+    behind a short spin kernel so that the events time the GPU's execution of
+    the K steps, not the host's submission of the first graph.  Returns
+    microseconds per step."""
     import torch
     if not graph:
         torch.cuda.synchronize()
@@ -275,6 +284,7 @@ def time_graph(fn, steps_per_round: int, K: int, label: str, graph: bool = True)
     g_tail = capture(tail) if tail else None
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(LEAD_CYCLES)
     ev0.record()
     for _ in range(full):
         g_full.replay()
