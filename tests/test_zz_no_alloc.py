@@ -78,6 +78,11 @@ def test_noalloc_matches_workspace_decode(P):
     # scratch region grows), then one token again on the grown region
     _compare(P, L8, to_device(layer8.x_dec[[2]], "bf16"), tx8, ts8, "8b b1")
     _compare(P, L8, to_device(layer8.x_dec[list(range(8))], "bf16"), tx8, ts8, "8b b8 grouped")
+    # the same layer with its channel-major proxy copy: the groups' Stage 1
+    # then runs from it (no scratch beyond the masks)
+    L8.add_proxy_qt()
+    _compare(P, L8, to_device(layer8.x_dec[list(range(8))], "bf16"), tx8, ts8, "8b b8 channel-major")
+    _compare(P, L8, to_device(layer8.x_dec[[1, 4, 6]], "bf16"), tx8, ts8, "8b b3 channel-major")
     _compare(P, L8, to_device(layer8.x_dec[[5]], "bf16"), tx8, ts8, "8b b1 again")
 
 
