@@ -520,15 +520,23 @@ size_t proxy_qt_bytes(int d, int f) {
 
 namespace {
 
+constexpr int kMaxDevices = 64;  // per-device state below (device ids past it share slot 0)
+
+int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices ? dev : 0;
+}
+
 template <typename T, bool kW, int kU>
 hipError_t qt_go(const QtArgs& a, size_t smem, hipStream_t s) {
-  // dynamic LDS past 64 KB must be allowed once per kernel
-  static std::atomic<size_t> allowed{0};
-  if (smem > 65536 && allowed.load() < smem) {
+  // dynamic LDS past 64 KB must be allowed once per kernel and device
+  static std::atomic<size_t> allowed[kMaxDevices];
+  const int dev = current_device();
+  if (smem > 65536 && allowed[dev].load() < smem) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(stage1_qt_kernel<T, kW, kU>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
-    allowed.store(smem);
+    allowed[dev].store(smem);
   }
   hipLaunchKernelGGL((stage1_qt_kernel<T, kW, kU>), dim3(static_cast<unsigned>(a.nb)), dim3(kQtThreads), smem, s, a);
   return hipGetLastError();
@@ -540,10 +548,16 @@ hipError_t qt_go2(const QtArgs& a, bool write_state, size_t smem, hipStream_t s)
   return write_state ? qt_go<T, true, 2>(a, smem, s) : qt_go<T, false, 2>(a, smem, s);
 }
 
+// LDS bytes a block may use on the current device (queried once per device)
 int device_max_lds() {
-  int dev = 0, v = 65536;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-    return 65536;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 65536;
+  std::atomic<int>* slot = dev < kMaxDevices ? &cached[dev] : nullptr;
+  int v = slot ? slot->load() : 0;
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) return 65536;
+  if (slot) slot->store(v);
   return v;
 }
 
