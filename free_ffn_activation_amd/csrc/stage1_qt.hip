@@ -17,10 +17,9 @@
 //     operand (lane l: channel l % 16, rows 32 (l / 16) .. + 31), so a wave
 //     streams its channels in contiguous 1 KB loads whose addresses do not
 //     depend on x: the weight stream starts with the kernel.  The images are
-//     stored chunk-major (chunk k of every group, then chunk k + 1): the
-//     blocks advance through their chunks together, so at any moment their
-//     reads cover one contiguous span spread over all HBM channels, rather
-//     than points a fixed power-of-two stride apart.
+//     stored chunk-major (chunk k of every group, then chunk k + 1), so the
+//     blocks, which advance through their chunks together, read one
+//     contiguous span at a time.
 //   * one 1024-thread block per CU owns a range of 16-channel groups over the
 //     whole input range: no K-split partials, no hand-off between blocks.  A
 //     group's input range is cut into `parts` ranges, one streaming wave per
