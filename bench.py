@@ -242,12 +242,21 @@ class Outs:
 # replays, so the host's submission latency of the first graph (tens of us)
 # is not counted as GPU time of the K steps.
 LEAD_CYCLES = 1_000_000
+# Untimed replays of the timed graphs right before the timed region (the
+# warm-up steps): measured on the 8B layer, a 20-step window timed right
+# after setup read 33.6 us per step and 32.5 us after other GPU work (a
+# 20-step bench run: 33.7 us without these replays, 33.0 us after 256).  The
+# warm replays end on the window's last steps, whose data the first timed
+# steps do not read, so no timed step finds its weights in a cache because
+# of them.
+WARM_STEPS = 256
 
 
 def time_graph(fn, steps_per_round: int, K: int, label: str, graph: bool = True) -> float:
     """Exactly K steps (fn(0) .. fn(K-1)) replayed from HIP graphs (whole
     rotations of steps_per_round steps, then a graph of the first
-    K mod steps_per_round), bracketed by HIP events on the current stream,
+    K mod steps_per_round), after at least WARM_STEPS untimed steps replayed
+    from the same graphs, bracketed by HIP events on the current stream,
     behind a short spin kernel so that the events time the GPU's execution of
     the K steps, not the host's submission of the first graph.  Returns
     microseconds per step."""
@@ -282,6 +291,9 @@ def time_graph(fn, steps_per_round: int, K: int, label: str, graph: bool = True)
     full, tail = divmod(K, steps_per_round)
     g_full = capture(steps_per_round) if full else None
     g_tail = capture(tail) if tail else None
+    warm = g_full if g_full is not None else g_tail
+    for _ in range(max(1, -(-WARM_STEPS // (steps_per_round if g_full is not None else tail)))):
+        warm.replay()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(LEAD_CYCLES)
