@@ -36,6 +36,30 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte global load with the non-temporal hint (global_load_dwordx4 ... nt),
+// for weight streams that one launch reads exactly once per address: the
+// lines are not kept as recently used in L2 and the Infinity Cache.  Measured
+// on MI355X (graph-replayed, one token per launch): the up/gate kernel 13.43
+// -> 12.15 us on the Qwen3-8B-shaped layer and 31.7 -> 28.9 us on the
+// Qwen3-32B-shaped one, Stage 1 10.45 -> 10.22 us.  Loads that re-read an
+// address within the launch stay on ldg16: with the hint each re-read went
+// to memory again (the down kernel's clamped batch slots: 8.16 -> 9.32 us;
+// per-token kernels over 8 tokens, whose kept rows and channels overlap:
+// 144.5 -> 155.9 us per step).
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return uint4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ u32x4_t ldg16v_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+// ldg16_nt for a launch over one token (kNt), ldg16 otherwise
+template <bool kNt>
+__device__ __forceinline__ uint4 ldg16_w(const void* p) {
+  if constexpr (kNt) return ldg16_nt(p);
+  else return ldg16(p);
+}
+
 // Two bf16 pairs multiplied and added into an fp32 accumulator
 // (v_dot2c_f32_bf16: products exact, fp32 sum).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {

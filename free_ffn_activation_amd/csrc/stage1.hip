@@ -21,7 +21,8 @@
 //   * main loop: 8 lanes cover one kept row's 128-byte slice (16 up + 16
 //     gate codes per lane, one 16-B load); each lane keeps 16 loads
 //     outstanding, so a wave's 128 rows (at 512 rows per split) go out in
-//     one batch; x and the two scales of a row are fetched in one round
+//     one batch (with the non-temporal hint when the launch covers one
+//     token); x and the two scales of a row are fetched in one round
 //     trip.  Rejected rows are never touched, so the bytes read are
 //     k_x * panel width per panel.
 //   * INT4 unpack: a nibble masked into the low 10 bits of a half word is an
@@ -93,7 +94,10 @@ __device__ __forceinline__ void acc_dword(float* acc, uint32_t w, float a24, flo
   acc[7] = fmaf(a20, static_cast<float>(h3.y), acc[7]);
 }
 
-template <typename T, bool kWriteState>
+// kNt: the gather loads carry the non-temporal hint (a launch over one token
+// reads each kept row's slice once; over several tokens the rows they share
+// are read once per token and stay cacheable).
+template <typename T, bool kWriteState, bool kNt>
 __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   constexpr int kPw = kS1Pw;
   constexpr int kLpr = kS1Lpr;
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
     for (int u = 0; u < kS1Unroll; ++u) off[u] = ko[u];
     uint4 w[kS1Unroll];
 #pragma unroll
-    for (int u = 0; u < kS1Unroll; ++u) w[u] = ldg16(qbase + (off[u] + coff));
+    for (int u = 0; u < kS1Unroll; ++u) w[u] = ldg16_w<kNt>(qbase + (off[u] + coff));
     __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
     const KeptA* kb = ka + rb + wslot;
     KeptA cur = kb[0];
@@ -321,6 +325,14 @@ __global__ __launch_bounds__(kS1Threads) void stage1_kernel(Stage1Args a) {
   }
 }
 
+template <typename T, bool kWriteState>
+void launch_stage1_t(const Stage1Args& a, dim3 grid, size_t smem, hipStream_t s) {
+  if (grid.y == 1)  // one token: every kept row's slice is read once (non-temporal loads)
+    hipLaunchKernelGGL((stage1_kernel<T, kWriteState, true>), grid, dim3(kS1Threads), smem, s, a);
+  else
+    hipLaunchKernelGGL((stage1_kernel<T, kWriteState, false>), grid, dim3(kS1Threads), smem, s, a);
+}
+
 }  // namespace
 
 hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_state,
@@ -333,14 +345,14 @@ hipError_t launch_stage1(const Stage1Args& a, int wdtype, int batch, bool write_
   const size_t smem = kept_bytes > red_bytes ? kept_bytes : red_bytes;
   if (wdtype == PROX_BF16) {
     if (write_state)
-      hipLaunchKernelGGL((stage1_kernel<Bf16Tag, true>), grid, dim3(kS1Threads), smem, s, a);
+      launch_stage1_t<Bf16Tag, true>(a, grid, smem, s);
     else
-      hipLaunchKernelGGL((stage1_kernel<Bf16Tag, false>), grid, dim3(kS1Threads), smem, s, a);
+      launch_stage1_t<Bf16Tag, false>(a, grid, smem, s);
   } else {
     if (write_state)
-      hipLaunchKernelGGL((stage1_kernel<F32Tag, true>), grid, dim3(kS1Threads), smem, s, a);
+      launch_stage1_t<F32Tag, true>(a, grid, smem, s);
     else
-      hipLaunchKernelGGL((stage1_kernel<F32Tag, false>), grid, dim3(kS1Threads), smem, s, a);
+      launch_stage1_t<F32Tag, false>(a, grid, smem, s);
   }
   return hipGetLastError();
 }

@@ -84,6 +84,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// the code stream: cache-policy operand 2 is the non-temporal hint (each code
+// chunk is read once per launch; x and the scales, which every block reads,
+// keep the default policy)
+__device__ __forceinline__ u32x4_t bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): the streaming waves end
 // their branch with it, so the second branch starts with no code load in
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(kQtThreads) void stage1_qt_kernel(QtArgs a) {
 #pragma unroll
       for (int k = 0; k < kUpw; ++k)
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) cw[c][k][pr] = bload16(qr, code_off(k, c, pr));
+        for (int pr = 0; pr < 2; ++pr) cw[c][k][pr] = bload16_nt(qr, code_off(k, c, pr));
     __builtin_amdgcn_sched_barrier(0);
     finish_pre();
     __syncthreads();  // staged x, scales and statistics in LDS
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(kQtThreads) void stage1_qt_kernel(QtArgs a) {
 #pragma unroll
       for (int k = 0; k < kUpw; ++k)
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) cw[c][k][pr] = bload16(qr, code_off(k, c, pr));
+        for (int pr = 0; pr < 2; ++pr) cw[c][k][pr] = bload16_nt(qr, code_off(k, c, pr));
     const int q = lane >> 4;
     const float un0 = ldexpf(1.0f, token_exp(2 * q) - 15);
     const float un1 = ldexpf(1.0f, token_exp(2 * q + 1) - 15);
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(kQtThreads) void stage1_qt_kernel(QtArgs a) {
               const f16x8_t av = __builtin_bit_cast(f16x8_t, af[(2 * s + pr) * 64 + ((lane ^ (s & 1)) - lane)]);
               C[k][pr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, codes_to_f16(w[s]), C[k][pr], 0, 0, 0);
             }
-            cw[kk][k][pr] = bload16(qr, code_off(k, c + kD, pr));
+            cw[kk][k][pr] = bload16_nt(qr, code_off(k, c + kD, pr));
           }
         }
         __syncthreads();  // this image read, the next one built

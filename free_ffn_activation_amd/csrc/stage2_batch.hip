@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void upgate_batch_kernel(UpGateBatchArgs 
     const bool won = k0 + unit * 8 < d;
 #pragma unroll
     for (int q = 0; q < kUgbRowsPerThread; ++q)
-      wv[q] = won ? *reinterpret_cast<const u32x4_t*>(wsrc[q] + k0 + unit * 8) : z;
+      wv[q] = won ? ldg16v_nt(wsrc[q] + k0 + unit * 8) : z;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int xu = (tid & 31) + 32 * q;

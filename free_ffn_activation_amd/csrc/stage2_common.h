@@ -128,11 +128,13 @@ struct WaveBitmap {
 // then publishes it; the function returns k_s); every wave writes its
 // ordinal's entry of the ascending index list; s_j is stored by channel index.  List mode: the
 // channel comes from the caller's list and s_j is stored by list position.
-// The block also zeroes its share of y (the down projection accumulates into
-// it).  s_j and the zeros of y are written with agent-coherent stores, so a
+// kNt: the weight runs are read with the non-temporal hint (a launch over one
+// token reads each run once; over several tokens the runs of channels they
+// share are read once per token and stay cacheable).  The block also zeroes
+// its share of y (the down projection accumulates into it).  s_j and the zeros of y are written with agent-coherent stores, so a
 // later phase of the same launch on another XCD can read them once the writer
 // has waited for its stores (see the fused kernel).  smem holds x (d elements).
-template <typename T, bool kFromBitmap, int kThreadsPB, bool kPublishCount = true>
+template <typename T, bool kFromBitmap, int kThreadsPB, bool kPublishCount = true, bool kNt = true>
 __device__ __forceinline__ int upgate_block(const UpGateArgs& a, int block, int nblocks, int b, uint8_t* smem) {
   typedef typename T::storage S;
   constexpr int kEpl = 16 / sizeof(S);  // elements per 16-byte load
@@ -192,8 +194,8 @@ __device__ __forceinline__ int upgate_block(const UpGateArgs& a, int block, int 
 #pragma unroll
         for (int u = 0; u < kUpGateUnroll; ++u) {
           const int cidx = min((s0 + u) * 64 + lane, nchunks - 1);
-          lu[u] = ldg16(wu + cidx);
-          lg[u] = ldg16(wg + cidx);
+          lu[u] = ldg16_w<kNt>(wu + cidx);
+          lg[u] = ldg16_w<kNt>(wg + cidx);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -219,8 +221,8 @@ __device__ __forceinline__ int upgate_block(const UpGateArgs& a, int block, int 
 #pragma unroll
     for (int u = 0; u < kUpGateUnroll; ++u) {
       const int cidx = min(u * 64 + lane, nchunks - 1);
-      lu[u] = ldg16(wu + cidx);
-      lg[u] = ldg16(wg + cidx);
+      lu[u] = ldg16_w<kNt>(wu + cidx);
+      lg[u] = ldg16_w<kNt>(wg + cidx);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -320,27 +322,27 @@ __device__ __forceinline__ int compact_range(uint32_t word, int c0, int c1, int*
 }
 
 // One batch of W_down rows for wave `wave`: rows i0 + u * kWaves of the list
-// (u < kDownUnroll), loads unconditional (a slot past the end re-reads the
+// (u < kU), loads unconditional (a slot past the end re-reads the
 // last row, a lane past the last column reads the slice's first column) so the
 // compiler can wait on them one by one.  Wd is the uniform base; row_bytes and
 // col_bytes give 32-bit byte offsets (W_down stays below 4 GiB for every
 // supported shape: 65536 x 12288 x 4 bytes is 3 GiB).
-template <int kWaves>
+template <int kWaves, int kU = kDownUnroll>
 __device__ __forceinline__ void down_batch_loads(const uint8_t* Wd, uint32_t row_bytes, uint32_t col_bytes,
-                                                 const int* jr, int n, int i0, uint4 (&w)[kDownUnroll]) {
+                                                 const int* jr, int n, int i0, uint4 (&w)[kU]) {
 #pragma unroll
-  for (int u = 0; u < kDownUnroll; ++u) {
+  for (int u = 0; u < kU; ++u) {
     const int i = min(i0 + u * kWaves, n - 1);
     const int j = jr[i];
     w[u] = ldg16(Wd + (static_cast<uint32_t>(j >= 0 ? j : 0) * row_bytes + col_bytes));
   }
 }
 
-template <typename T, int kWaves>
+template <typename T, int kWaves, int kU = kDownUnroll>
 __device__ __forceinline__ void down_batch_fma(float* acc, const int* jr, const float* sr, int n, int i0, bool cvalid,
-                                               const uint4 (&w)[kDownUnroll]) {
+                                               const uint4 (&w)[kU]) {
 #pragma unroll
-  for (int u = 0; u < kDownUnroll; ++u) {
+  for (int u = 0; u < kU; ++u) {
     const int i = min(i0 + u * kWaves, n - 1);
     const float sv = (i0 + u * kWaves < n && jr[i] >= 0 && cvalid) ? sr[i] : 0.f;
     axpy16<T>(acc, sv, w[u]);

@@ -20,7 +20,8 @@
 //     block 0 publishes k_s, and every wave writes its ordinal's index.  List
 //     mode: the channel is read from the caller's list.
 //   * 64 lanes x 16 B per load cover 512 bf16 of a run; up to 8 steps (16
-//     loads, 16 KB per wave) are issued before use.  x is staged in LDS once
+//     loads, 16 KB per wave) are issued before use, with the non-temporal
+//     hint when the launch covers one token (each run is then read once).  x is staged in LDS once
 //     per block; the block's one barrier comes after the first weight loads
 //     are issued, so it overlaps the gather.  bf16 products use
 //     v_dot2_f32_bf16 (exact products, fp32 sum).
@@ -33,11 +34,20 @@
 namespace prox {
 namespace {
 
-template <typename T, bool kFromBitmap>
+template <typename T, bool kFromBitmap, bool kNt>
 __global__ __launch_bounds__(kUgThreads) void upgate_kernel(UpGateArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  s2::upgate_block<T, kFromBitmap, kUgThreads>(a, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x),
-                                               static_cast<int>(blockIdx.y), smem);
+  s2::upgate_block<T, kFromBitmap, kUgThreads, true, kNt>(a, static_cast<int>(blockIdx.x),
+                                                          static_cast<int>(gridDim.x),
+                                                          static_cast<int>(blockIdx.y), smem);
+}
+
+template <typename T, bool kFromBitmap>
+void launch_upgate_t(const UpGateArgs& a, dim3 grid, size_t smem, hipStream_t s) {
+  if (grid.y == 1)  // one token: every weight run is read once (non-temporal loads)
+    hipLaunchKernelGGL((upgate_kernel<T, kFromBitmap, true>), grid, dim3(kUgThreads), smem, s, a);
+  else
+    hipLaunchKernelGGL((upgate_kernel<T, kFromBitmap, false>), grid, dim3(kUgThreads), smem, s, a);
 }
 
 }  // namespace
@@ -49,14 +59,14 @@ hipError_t launch_upgate(const UpGateArgs& a, int wdtype, int batch, int blocks,
   const size_t smem = static_cast<size_t>(a.d) * esz;
   if (wdtype == PROX_BF16) {
     if (from_bitmap)
-      hipLaunchKernelGGL((upgate_kernel<Bf16Tag, true>), grid, dim3(kUgThreads), smem, s, a);
+      launch_upgate_t<Bf16Tag, true>(a, grid, smem, s);
     else
-      hipLaunchKernelGGL((upgate_kernel<Bf16Tag, false>), grid, dim3(kUgThreads), smem, s, a);
+      launch_upgate_t<Bf16Tag, false>(a, grid, smem, s);
   } else {
     if (from_bitmap)
-      hipLaunchKernelGGL((upgate_kernel<F32Tag, true>), grid, dim3(kUgThreads), smem, s, a);
+      launch_upgate_t<F32Tag, true>(a, grid, smem, s);
     else
-      hipLaunchKernelGGL((upgate_kernel<F32Tag, false>), grid, dim3(kUgThreads), smem, s, a);
+      launch_upgate_t<F32Tag, false>(a, grid, smem, s);
   }
   return hipGetLastError();
 }
