@@ -80,7 +80,7 @@ KERNELS = {
     "stage1_proxy": (("stage1.hip",), ("stage1_kernel<prox::Bf16Tag, false, true>",)),
     "stage2_fused": (("stage2_fused.hip", "stage2_common.h"), ("stage2_fused_kernel<prox::Bf16Tag>",)),
     "stage2_upgate": (("stage2_upgate.hip", "stage2_common.h"), ("upgate_kernel<prox::Bf16Tag, true, true>",)),
-    "stage2_down": (("stage2_down.hip", "stage2_common.h"), ("down_kernel<prox::Bf16Tag, true>",)),
+    "stage2_down": (("stage2_down.hip", "stage2_common.h"), ("down_kernel<prox::Bf16Tag, true, true>",)),
     "stage1_proxy_batch": (("stage1_qt.hip", "stage1_mfma.h"), ("stage1_qt_kernel<prox::Bf16Tag, false, 1>",)),
     "stage2_upgate_batch": (("stage2_batch.hip",), ("upgate_batch_kernel",)),
     "stage2_down_batch": (("stage2_batch.hip",), ("down_batch_kernel", "down_reduce_kernel")),

@@ -43,9 +43,10 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
 // -> 12.15 us on the Qwen3-8B-shaped layer and 31.7 -> 28.9 us on the
 // Qwen3-32B-shaped one, Stage 1 10.45 -> 10.22 us.  Loads that re-read an
 // address within the launch stay on ldg16: with the hint each re-read went
-// to memory again (the down kernel's clamped batch slots: 8.16 -> 9.32 us;
-// per-token kernels over 8 tokens, whose kept rows and channels overlap:
-// 144.5 -> 155.9 us per step).
+// to memory again (the down kernel's batch slots past the list end, when they
+// re-read its last row: 8.16 -> 9.32 us; per-token kernels over 8 tokens,
+// whose kept rows and channels overlap: 144.5 -> 155.9 us per step).  The
+// down kernels instead point such slots past their buffer's records.
 __device__ __forceinline__ uint4 ldg16_nt(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return uint4{v.x, v.y, v.z, v.w};
@@ -53,6 +54,17 @@ __device__ __forceinline__ uint4 ldg16_nt(const void* p) {
 __device__ __forceinline__ u32x4_t ldg16v_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
+// A weight matrix of rows x cols elements of es bytes (below 4 GiB for every
+// supported shape) as a raw buffer resource.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* w, int rows, int cols, int es) {
+  const uint32_t bytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(cols) * static_cast<uint32_t>(es);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(w), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000 /* raw buffer, 32-bit data */);
+}
+// An offset past the records of every weight_rsrc buffer: a load from it
+// returns zeros without a memory access.
+constexpr uint32_t kWeightOob = 0xFFFFFF00u;
+
 // ldg16_nt for a launch over one token (kNt), ldg16 otherwise
 template <bool kNt>
 __device__ __forceinline__ uint4 ldg16_w(const void* p) {

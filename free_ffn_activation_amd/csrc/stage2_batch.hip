@@ -372,15 +372,20 @@ __global__ __launch_bounds__(kDnbThreads) void down_batch_kernel(DownBatchArgs a
   const int unit = tid & 63;
   const int col0 = cs * kDnbCols;
   const bool col_ok = col0 + unit * 8 < d;
-  const uint16_t* W = static_cast<const uint16_t*>(a.w_down);
   u32x4_t ld[kDnbPrefetch][4];
-  const u32x4_t z = {0u, 0u, 0u, 0u};
+  // W_down through a buffer resource with the non-temporal hint (each row
+  // slice is read once per launch); the last tile's padding rows and columns
+  // past d load from past the buffer's records: zeros, no memory access
+  const __amdgpu_buffer_rsrc_t wr = weight_rsrc(a.w_down, f, d, 2);
   auto issue = [&](int kt, u32x4_t (&dst)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = kt * kDnbTileRows + (tid >> 6) + 8 * q;
       const int ch = ul[min(r, nr - 1)];
-      dst[q] = col_ok ? *reinterpret_cast<const u32x4_t*>(W + static_cast<size_t>(ch) * d + col0 + unit * 8) : z;
+      const uint32_t off =
+          (r < nr && col_ok) ? (static_cast<uint32_t>(ch) * static_cast<uint32_t>(d) + static_cast<uint32_t>(col0 + unit * 8)) * 2u
+                             : kWeightOob;
+      dst[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2 /* nt */));
     }
   };
 #pragma unroll

@@ -14,17 +14,23 @@
 //     so no count or list has to be fetched first; with a caller-given list a
 //     row group is a contiguous range of that list.  The block stages its
 //     (index, s_j) pairs in LDS; each of its 16 waves streams every 16th row
-//     with 8 loads in flight and accumulates its columns in registers.
+//     with 8 (or, for its last 4 rows or fewer, 4) loads in flight and
+//     accumulates its columns in registers.  The loads go through a buffer
+//     resource (with the non-temporal hint when the launch covers one
+//     token); batch slots past the list end read past the buffer's records
+//     (zeros, no memory access).
 //   * the 16 waves' partial rows are summed through LDS and the block adds its
 //     slice into y with fp32 atomics (y was zeroed by the up/gate kernel).
 //     Large blocks keep the atomic count (row groups x d) low: fp32 global
 //     atomics cost far more per byte than the weight stream.
+#include <type_traits>
+
 #include "stage2_common.h"
 
 namespace prox {
 namespace {
 
-template <typename T, bool kFromBitmap>
+template <typename T, bool kFromBitmap, bool kNt>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
   typedef typename T::storage S;
   constexpr int kEpl = 16 / sizeof(S);
@@ -76,31 +82,37 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DownArgs a) {
 
   const int col = cs * kCw + lane * kEpl;
   const bool cvalid = col < d;
-  const uint8_t* Wd = static_cast<const uint8_t*>(a.w_down);
+  const __amdgpu_buffer_rsrc_t wr = weight_rsrc(a.w_down, f, d, static_cast<int>(sizeof(S)));
   float acc[kEpl];
 #pragma unroll
   for (int e = 0; e < kEpl; ++e) acc[e] = 0.f;
   const int colc = cvalid ? col : cs * kCw;
   const uint32_t row_bytes = static_cast<uint32_t>(d * sizeof(S));
   const uint32_t col_bytes = static_cast<uint32_t>(colc * sizeof(S));
-  // A wave with at most half a batch of rows left issues a half batch: the
-  // clamped slots of a full one re-read the last row (at ~56 kept rows per
-  // row group of the Qwen3-8B-shaped layer, 4.5 of a wave's 8 loads were such
-  // re-reads; 8.16 -> 7.93 us measured)
+  auto batch = [&](int i0, auto depth) {
+    constexpr int kU = decltype(depth)::value;
+    uint4 w[kU];
+    s2::down_batch_loads_buf<kWaves, kU, kNt>(wr, row_bytes, col_bytes, jr, n, i0, w);
+    __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
+    s2::down_batch_fma<T, kWaves, kU>(acc, jr, sr, n, i0, cvalid, w);
+  };
+  // A wave with at most half a batch of rows left issues a half batch (at
+  // ~56 kept rows per row group of the Qwen3-8B-shaped layer a wave has 3-4)
   for (int i0 = wave; i0 < n; i0 += kWaves * kDownUnroll) {
-    if (i0 + (kDownUnroll / 2) * kWaves >= n) {  // wave-uniform
-      uint4 w[kDownUnroll / 2];
-      s2::down_batch_loads<kWaves, kDownUnroll / 2>(Wd, row_bytes, col_bytes, jr, n, i0, w);
-      __builtin_amdgcn_sched_barrier(0);
-      s2::down_batch_fma<T, kWaves, kDownUnroll / 2>(acc, jr, sr, n, i0, cvalid, w);
-    } else {
-      uint4 w[kDownUnroll];
-      s2::down_batch_loads<kWaves>(Wd, row_bytes, col_bytes, jr, n, i0, w);
-      __builtin_amdgcn_sched_barrier(0);  // the batch stays in flight together
-      s2::down_batch_fma<T, kWaves>(acc, jr, sr, n, i0, cvalid, w);
-    }
+    if (i0 + (kDownUnroll / 2) * kWaves >= n)  // wave-uniform
+      batch(i0, std::integral_constant<int, kDownUnroll / 2>{});
+    else
+      batch(i0, std::integral_constant<int, kDownUnroll>{});
   }
   s2::down_reduce_add<kDownThreads, kCw>(red, acc, kEpl, cs, d, a.y + static_cast<size_t>(b) * d);
+}
+
+template <typename T, bool kFromBitmap>
+void launch_down_t(const DownArgs& a, dim3 grid, size_t smem, hipStream_t s) {
+  if (grid.y == 1)  // one token: every row slice is read once (non-temporal loads)
+    hipLaunchKernelGGL((down_kernel<T, kFromBitmap, true>), grid, dim3(kDownThreads), smem, s, a);
+  else
+    hipLaunchKernelGGL((down_kernel<T, kFromBitmap, false>), grid, dim3(kDownThreads), smem, s, a);
 }
 
 }  // namespace
@@ -111,14 +123,14 @@ hipError_t launch_down(const DownArgs& a, int wdtype, int batch, bool from_bitma
   const size_t smem = static_cast<size_t>(kDownThreads / 64) * cw * 4 + static_cast<size_t>(a.max_rows) * 8;
   if (wdtype == PROX_BF16) {
     if (from_bitmap)
-      hipLaunchKernelGGL((down_kernel<Bf16Tag, true>), grid, dim3(kDownThreads), smem, s, a);
+      launch_down_t<Bf16Tag, true>(a, grid, smem, s);
     else
-      hipLaunchKernelGGL((down_kernel<Bf16Tag, false>), grid, dim3(kDownThreads), smem, s, a);
+      launch_down_t<Bf16Tag, false>(a, grid, smem, s);
   } else {
     if (from_bitmap)
-      hipLaunchKernelGGL((down_kernel<F32Tag, true>), grid, dim3(kDownThreads), smem, s, a);
+      launch_down_t<F32Tag, true>(a, grid, smem, s);
     else
-      hipLaunchKernelGGL((down_kernel<F32Tag, false>), grid, dim3(kDownThreads), smem, s, a);
+      launch_down_t<F32Tag, false>(a, grid, smem, s);
   }
   return hipGetLastError();
 }
