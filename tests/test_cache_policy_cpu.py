@@ -25,7 +25,31 @@ import re
 
 import pytest
 
-from test_handoff_cpu import _device_asm, _hipcc, _kernel_bodies
+from test_handoff_cpu import _device_asm, _hipcc
+
+
+def _kernel_bodies(asm: str, name_part: str):
+    """{symbol: [instruction lines]} of every kernel whose symbol contains
+    name_part, the whole function (its early-exit blocks may come before the
+    main loop in the layout, so the body runs to the function's end label, not
+    to the first s_endpgm)."""
+    bodies, cur = {}, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            cur = [] if name_part in m.group(1) else None
+            if cur is not None:
+                bodies[m.group(1)] = cur
+            continue
+        if line.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        if cur is None:
+            continue
+        ins = line.split(";")[0].strip()
+        if ins and not ins.startswith(".") and not ins.endswith(":"):
+            cur.append(ins)
+    return bodies
 
 # (source, kernel-name substring, least number of 16-byte nt loads in the
 # one-token instantiation: one gather batch of the kernel)
