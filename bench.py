@@ -245,11 +245,12 @@ LEAD_CYCLES = 1_000_000
 # Untimed replays of the timed graphs right before the timed region (the
 # warm-up steps): measured on the 8B layer, a 20-step window timed right
 # after setup read 33.6 us per step and 32.5 us after other GPU work (a
-# 20-step bench run: 33.7 us without these replays, 33.0 us after 256).  The
-# warm replays end on the window's last steps, whose data the first timed
-# steps do not read, so no timed step finds its weights in a cache because
-# of them.
-WARM_STEPS = 256
+# 20-step bench run: 33.7 us without these replays, 33.0 us after 256; with
+# the current kernels three 20-step runs read 30.57 / 30.72 / 30.50 us after
+# 256 and 30.36 / 30.54 / 30.43 us after 1024).  The warm replays end on the
+# window's last steps, whose data the first timed steps do not read, so no
+# timed step finds its weights in a cache because of them.
+WARM_STEPS = 1024
 
 
 def time_graph(fn, steps_per_round: int, K: int, label: str, graph: bool = True) -> float:
